@@ -1,0 +1,304 @@
+"""CPU oracle for group-wise weight-only RTN quantization, the layout-v1 packed
+stream, dequantization, and the dequantize-GEMV/GEMM that consumes it.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, plain, obviously-correct
+statement of what the GPU library computes.  Only the test suite, the smoke
+check in ``__graft_entry__.smoke`` and the ``cpu_baseline`` leg of ``bench.py``
+may import it.  The product path (the HIP library and its Python binding)
+never imports, calls or links anything here, and this module imports nothing
+from the product.
+
+Sources (the five pages on weight-only quantization):
+
+* "Quantising Large Language Models for Efficient Inference", section
+  "Post-training methods for 4-bit weights": symmetric group-wise quantisation
+  of a weight row (scale = max|w| / qmax per group, q = clip(round(w/scale),
+  -qmax-1, qmax), dequant q*scale); one scale (and zero point) per group of
+  64-128 weights.
+* "CMU 11-868 L19-L20 Model Quantization", section "absmax and zero-point":
+  absmax and zero-point quantizers; a zero range is replaced by 1; the
+  zero-point is a rounded integer offset; dequant is (q - zp) / scale.
+* "LLM Quantization: 160GB Model on a Laptop", sections "Symmetric
+  Quantization" (scale = max_abs / (2^(bits-1) - 1), round(value/scale),
+  quantized*scale, worked example) and "Asymmetric Quantization"
+  (scale = (max - min) / (qmax - qmin)).
+* "Quantising Large Language Models ...", section "Why LLMs are hard to
+  quantise": the per-channel scaling identity Y = (X diag(s)^-1)(diag(s) W);
+  "MIT 6.5940 Lab 4 + Lab 5", Lab 4 Question 2: multiply a salient weight
+  channel by s and divide the activation by s.
+* "MIT 6.5940 Lab 4 + Lab 5", Lab 4 "Starting point and setup": pseudo
+  quantization = quantize to integers then dequantize immediately.
+* "Quantising Large Language Models ...", section "Weight-only vs
+  weight-and-activation quantisation": W4A16 weights are dequantised on the
+  fly inside the matrix-multiplication kernel.
+
+Readings taken where the pages leave a step open (each is listed, with its
+reason, in the design notes of the repository):
+
+* Rounding is round-half-to-even (numpy ``rint``), as in the numpy and torch
+  snippets; the JavaScript snippet's half-up rounding is not used.
+* Arithmetic that decides a stored value (scale, zero-point, code) is IEEE
+  binary32, one correctly-rounded operation per step, the precision the GPU
+  kernel uses; the scale is stored as IEEE binary16 (round-to-nearest-even,
+  subnormals kept) and the codes are computed with the stored scale.
+* Symmetric codes are clipped to [-2^(b-1), 2^(b-1)-1] and stored unsigned as
+  u = q + 2^(b-1); an all-zero group (scale 0) stores u = 2^(b-1).
+* Asymmetric: range r = max - min (replaced by 1 when 0), S = f16(r/(2^b-1)),
+  zero-point Z = clip(rne(-min/S), 0, 2^b-1) (an integer, stored in fp16),
+  u = clip(rne(w/S) + Z, 0, 2^b-1); a scale that underflows to 0 gives Z = 0
+  and u = 0.
+* The AWQ fold multiplies W[n,k] by s[k] in binary32 before the group
+  statistics; the GEMV/GEMM divides x by s (exactly, in fp64, here).
+* Dequantization and products are exact / fp64: w_hat = (u - Z) * S.
+
+Parity pins for every function here live in ``tests/test_oracle.py``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "Quantized",
+    "fold_act_scale",
+    "quantize",
+    "pack_v1",
+    "unpack_v1",
+    "packed_row_bytes",
+    "dequantize",
+    "bf16_bits_to_f64",
+    "activations_f64",
+    "gemm",
+    "quantize_pack",
+    "rel_l2",
+]
+
+
+@dataclass
+class Quantized:
+    """Result of group-wise RTN quantization of an [N, K] weight matrix.
+
+    codes  : uint8 [N, K], unsigned codes u in [0, 2^bits - 1]
+    scales : float16 [N, K // group_size]
+    zeros  : float16 [N, K // group_size] (asymmetric) or None (symmetric:
+             the implied zero is 2^(bits-1))
+    """
+
+    codes: np.ndarray
+    scales: np.ndarray
+    zeros: Optional[np.ndarray]
+    bits: int
+    group_size: int
+    asymmetric: bool
+
+
+def fold_act_scale(W: np.ndarray, act_scale: Optional[np.ndarray]) -> np.ndarray:
+    """AWQ fold: w'[n, k] = fl32(W[n, k] * s[k]).
+
+    Follows the per-channel scaling identity of "Quantising Large Language
+    Models ...", section "Why LLMs are hard to quantise"
+    (Y = (X diag(s)^-1)(diag(s) W)), and Lab 4 Question 2 of "MIT 6.5940 Lab 4
+    + Lab 5" (scale a weight channel up by s, the activation down by s).
+    One binary32 multiply per weight; without a scale the fp16 weights are
+    widened exactly.
+    """
+    w = np.asarray(W).astype(np.float32)
+    if act_scale is None:
+        return w
+    s = np.asarray(act_scale, dtype=np.float32)
+    assert s.shape == (w.shape[1],)
+    return np.multiply(w, s[None, :], dtype=np.float32)
+
+
+def quantize(
+    W: np.ndarray,
+    bits: int,
+    group_size: int,
+    asymmetric: bool,
+    act_scale: Optional[np.ndarray] = None,
+) -> Quantized:
+    """Group-wise round-to-nearest quantization of W [N, K] (fp16 values).
+
+    Groups are ``group_size`` consecutive weights of one row along K, starting
+    at k = 0 (the reshape of "Quantising Large Language Models ...", section
+    "Post-training methods for 4-bit weights").
+
+    Symmetric (absmax): per group a = max|w|, S = f16(fl32(a / qmax)) with
+    qmax = 2^(bits-1) - 1 ("LLM Quantization: 160GB Model on a Laptop",
+    section "Symmetric Quantization"; "Quantising ..." group-wise code);
+    q = clip(rne(fl32(w / S)), -2^(bits-1), 2^(bits-1) - 1); u = q + 2^(bits-1).
+
+    Asymmetric (zero-point): r = fl32(max - min), r := 1 if r == 0 ("CMU
+    11-868 L19-L20", section "absmax and zero-point"); S = f16(fl32(r / qu))
+    with qu = 2^bits - 1 ("LLM Quantization ...", section "Asymmetric
+    Quantization"); Z = clip(rne(fl32(-min / S)), 0, qu);
+    u = clip(rne(fl32(w / S)) + Z, 0, qu).
+    """
+    W = np.asarray(W)
+    assert W.ndim == 2
+    N, K = W.shape
+    assert bits in (2, 3, 4, 8) and group_size > 0 and K % group_size == 0
+    w = fold_act_scale(W, act_scale)
+    g = w.reshape(N, K // group_size, group_size)
+
+    if not asymmetric:
+        half = 2 ** (bits - 1)
+        qmax = np.float32(half - 1)
+        a = np.abs(g).max(axis=2)
+        S = np.divide(a, qmax, dtype=np.float32).astype(np.float16)
+        S32 = S.astype(np.float32)[:, :, None]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = np.rint(np.divide(g, S32, dtype=np.float32))
+        q = np.where(S32 == 0, np.float32(0), q)
+        q = np.clip(q, -half, half - 1)
+        u = (q + half).astype(np.uint8)
+        return Quantized(u.reshape(N, K), S, None, bits, group_size, False)
+
+    qu = np.float32(2 ** bits - 1)
+    mn = g.min(axis=2)
+    mx = g.max(axis=2)
+    r = np.subtract(mx, mn, dtype=np.float32)
+    r = np.where(r == 0, np.float32(1), r).astype(np.float32)
+    S = np.divide(r, qu, dtype=np.float32).astype(np.float16)
+    S32 = S.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        Zf = np.rint(np.divide(-mn, S32, dtype=np.float32))
+        Zf = np.where(S32 == 0, np.float32(0), Zf)
+        Zf = np.clip(Zf, 0, qu)
+        q = np.rint(np.divide(g, S32[:, :, None], dtype=np.float32))
+    q = np.where(S32[:, :, None] == 0, -Zf[:, :, None], q)
+    u = np.clip(q + Zf[:, :, None], 0, qu).astype(np.uint8)
+    return Quantized(u.reshape(N, K), S, Zf.astype(np.float16), bits, group_size, True)
+
+
+def packed_row_bytes(K: int, bits: int) -> int:
+    """Bytes of one packed row: K * bits / 8."""
+    assert (K * bits) % 8 == 0
+    return K * bits // 8
+
+
+def pack_v1(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack unsigned codes [N, K] into layout v1, uint8 [N, K*bits/8].
+
+    Layout v1 (little-endian 32-bit words, rows back to back):
+
+    * 4-bit: word j of a row holds k in [8j, 8j+8); the code of
+      k = 8j + 2t + h (t in 0..3, h in 0..1) sits at bits [16h + 4t, 16h + 4t + 4).
+    * 3-bit: a 12-byte unit j (words w0, w1, w2) holds k in [32j, 32j+32); for
+      i = k - 32j = 2t + h (t in 0..15, h in 0..1) the two low bits of the
+      code sit in word w_(t // 8) at bits [16h + 2(t % 8), +2) and the high bit
+      in w2 at bit 16h + t.
+
+    Written element by element from that definition (slow on purpose).
+    """
+    codes = np.asarray(codes)
+    N, K = codes.shape
+    if bits == 4:
+        assert K % 8 == 0
+        words = np.zeros((N, K // 8), dtype=np.uint32)
+        for j in range(K // 8):
+            for t in range(4):
+                for h in range(2):
+                    k = 8 * j + 2 * t + h
+                    words[:, j] |= (codes[:, k].astype(np.uint32) & 0xF) << np.uint32(16 * h + 4 * t)
+    elif bits == 3:
+        assert K % 32 == 0
+        words = np.zeros((N, K // 32, 3), dtype=np.uint32)
+        for j in range(K // 32):
+            for i in range(32):
+                t, h = divmod(i, 2)
+                u = codes[:, 32 * j + i].astype(np.uint32)
+                words[:, j, t // 8] |= (u & 3) << np.uint32(16 * h + 2 * (t % 8))
+                words[:, j, 2] |= ((u >> 2) & 1) << np.uint32(16 * h + t)
+        words = words.reshape(N, -1)
+    else:
+        raise ValueError("layout v1 is defined for 3 and 4 bits")
+    return np.ascontiguousarray(words.astype("<u4")).view(np.uint8).reshape(N, packed_row_bytes(K, bits))
+
+
+def unpack_v1(packed: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """Inverse of :func:`pack_v1`: uint8 [N, K*bits/8] -> codes uint8 [N, K]."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    N = packed.shape[0]
+    words = packed.reshape(N, -1).view("<u4").astype(np.uint32)
+    codes = np.zeros((N, K), dtype=np.uint8)
+    if bits == 4:
+        for j in range(K // 8):
+            for t in range(4):
+                for h in range(2):
+                    codes[:, 8 * j + 2 * t + h] = (words[:, j] >> np.uint32(16 * h + 4 * t)) & 0xF
+    elif bits == 3:
+        words = words.reshape(N, K // 32, 3)
+        for j in range(K // 32):
+            for i in range(32):
+                t, h = divmod(i, 2)
+                lo = (words[:, j, t // 8] >> np.uint32(16 * h + 2 * (t % 8))) & 3
+                hi = (words[:, j, 2] >> np.uint32(16 * h + t)) & 1
+                codes[:, 32 * j + i] = lo | (hi << 2)
+    else:
+        raise ValueError("layout v1 is defined for 3 and 4 bits")
+    return codes
+
+
+def dequantize(q: Quantized) -> np.ndarray:
+    """Pseudo-quantization's second half: w_hat = (u - Z) * S, exact in fp64.
+
+    "MIT 6.5940 Lab 4 + Lab 5", Lab 4 setup (quantize then dequantize);
+    dequant formulas of "CMU 11-868 L19-L20" ((q - zp)/scale) and "Quantising
+    ..." (q * scale).  |u - Z| <= 2^bits - 1 and S has 11 significant bits, so
+    every product is exact in binary64.
+    """
+    N, K = q.codes.shape
+    G = q.group_size
+    S = np.repeat(q.scales.astype(np.float64), G, axis=1)
+    if q.zeros is None:
+        Z = np.float64(2 ** (q.bits - 1))
+    else:
+        Z = np.repeat(q.zeros.astype(np.float64), G, axis=1)
+    return (q.codes.astype(np.float64) - Z) * S
+
+
+def bf16_bits_to_f64(bits16: np.ndarray) -> np.ndarray:
+    """Exact value of bfloat16 numbers given as their uint16 bit patterns."""
+    b = np.asarray(bits16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def activations_f64(X: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact fp64 value of activations stored as fp16 values or bf16 bits."""
+    if dtype == "f16":
+        return np.asarray(X, dtype=np.float16).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_bits_to_f64(X)
+    raise ValueError(dtype)
+
+
+def gemm(X64: np.ndarray, w_hat: np.ndarray, act_scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """Y = (X diag(s)^-1) W_hat^T with fp64 accumulation.
+
+    X64 is [M, K] (exact fp64 values of the activations), w_hat [N, K].  With
+    an AWQ scale the activation is divided by s ("Quantising ...", section
+    "Why LLMs are hard to quantise"); the weights already carry the factor s.
+    A GEMV is the M = 1 case.
+    """
+    X64 = np.atleast_2d(np.asarray(X64, dtype=np.float64))
+    if act_scale is not None:
+        X64 = X64 / np.asarray(act_scale, dtype=np.float32).astype(np.float64)[None, :]
+    return X64 @ np.asarray(w_hat, dtype=np.float64).T
+
+
+def quantize_pack(W, bits, group_size, asymmetric, act_scale=None):
+    """quantize + pack_v1: returns (packed uint8 [N, K*bits/8], scales f16, zeros f16|None, Quantized)."""
+    q = quantize(W, bits, group_size, asymmetric, act_scale)
+    return pack_v1(q.codes, bits), q.scales, q.zeros, q
+
+
+def rel_l2(y: np.ndarray, y_ref: np.ndarray) -> float:
+    """||y - y_ref||_2 / ||y_ref||_2 over the whole output, in fp64."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    den = np.linalg.norm(y_ref.ravel())
+    num = np.linalg.norm((y - y_ref).ravel())
+    return float(num / den) if den > 0 else float(num)

@@ -1,0 +1,411 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages print, exact rational arithmetic, brute force over every code, closed
+forms and invariants.  None of these tests needs a GPU.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import woq_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f16(a):
+    return np.asarray(a, dtype=np.float32).astype(np.float16)
+
+
+def _random_groups(rng, N, K, std=0.02, outlier_frac=0.01):
+    w = rng.standard_normal((N, K)).astype(np.float32) * np.float32(std)
+    m = rng.random((N, K)) < outlier_frac
+    w[m] = rng.standard_normal(int(m.sum())).astype(np.float32) * np.float32(0.5)
+    return w.astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# Worked example printed on "LLM Quantization: 160GB Model on a Laptop",
+# section "Symmetric Quantization".
+# ---------------------------------------------------------------------------
+
+def test_worked_example_symmetric():
+    g = _load("worked_example_symmetric.json")
+    w = _f16(g["values"])[None, :]
+    q = O.quantize(w, g["bits"], len(g["values"]), asymmetric=False)
+    signed = q.codes.astype(int)[0] - 2 ** (g["bits"] - 1)
+    assert signed.tolist() == g["quantized"]
+    S = float(q.scales[0, 0])
+    tol = 0.5 * 10 ** -g["print_decimals"]
+    assert abs(S - g["scale_approx"]) <= tol
+    w_hat = O.dequantize(q)[0]
+    assert np.all(np.abs(w_hat - np.array(g["dequantized_approx"])) <= tol)
+    err = np.mean(np.abs(w_hat - w[0].astype(np.float64)) / np.abs(w[0].astype(np.float64)))
+    assert round(100 * err) == g["average_error_percent"]
+
+
+def test_worked_example_in_a_zero_padded_group_of_128():
+    # Zero padding changes neither the absmax nor the first six codes.
+    g = _load("worked_example_symmetric.json")
+    w = np.zeros((1, 128), np.float16)
+    w[0, :6] = _f16(g["values"])
+    q = O.quantize(w, 4, 128, asymmetric=False)
+    assert (q.codes[0, :6].astype(int) - 8).tolist() == g["quantized"]
+    assert np.all(q.codes[0, 6:] == 8)
+
+
+def test_worked_example_asymmetric_error_in_page_range():
+    # "LLM Quantization ...", section "Asymmetric Quantization": average error
+    # drops to 5-10% (a loose claim; our zero-point form lands inside it).
+    g = _load("worked_example_symmetric.json")
+    w = _f16(g["values"])[None, :]
+    q = O.quantize(w, 4, 6, asymmetric=True)
+    w_hat = O.dequantize(q)[0]
+    err = np.mean(np.abs(w_hat - w[0].astype(np.float64)) / np.abs(w[0].astype(np.float64)))
+    assert 0.05 <= err <= 0.10
+    assert q.codes.min() == 0  # the minimum lands on the bottom code
+
+
+# ---------------------------------------------------------------------------
+# Exact rational reference of the code decision (fp16 inputs, no fold).
+# For an fp16 w and an fp16 S the exact quotient is never within one binary32
+# rounding of a half-integer unless it is one, so rne(fl32(w/S)) equals the
+# exactly rounded quotient.
+# ---------------------------------------------------------------------------
+
+def _round_half_even(fr: Fraction) -> int:
+    return round(fr)  # Python rounds Fractions half-to-even
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("asym", [False, True])
+def test_codes_equal_exact_rational_rounding(bits, asym):
+    rng = np.random.default_rng(11 + bits + 10 * asym)
+    W = _random_groups(rng, 6, 256)
+    q = O.quantize(W, bits, 128, asym)
+    for n in range(W.shape[0]):
+        for gi in range(2):
+            S = Fraction(float(q.scales[n, gi]))
+            grp = [Fraction(float(v)) for v in W[n, 128 * gi:128 * (gi + 1)]]
+            if asym:
+                Z = _round_half_even(-min(grp) / S)
+                Z = min(max(Z, 0), 2 ** bits - 1)
+                assert float(q.zeros[n, gi]) == Z
+                ref = [min(max(_round_half_even(v / S) + Z, 0), 2 ** bits - 1) for v in grp]
+            else:
+                h = 2 ** (bits - 1)
+                ref = [min(max(_round_half_even(v / S), -h), h - 1) + h for v in grp]
+            assert q.codes[n, 128 * gi:128 * (gi + 1)].tolist() == ref
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("asym", [False, True])
+def test_scale_is_fp16_rounding_of_exact_ratio(bits, asym):
+    rng = np.random.default_rng(5 + bits)
+    W = _random_groups(rng, 8, 512)
+    q = O.quantize(W, bits, 128, asym)
+    g = W.astype(np.float64).reshape(8, 4, 128)
+    if asym:
+        exact = (g.max(2) - g.min(2)) / (2 ** bits - 1)
+    else:
+        exact = np.abs(g).max(2) / (2 ** (bits - 1) - 1)
+    S = q.scales.astype(np.float64)
+    # within half an fp16 ulp (plus the binary32 intermediate rounding)
+    ulp = np.spacing(q.scales).astype(np.float64)
+    assert np.all(np.abs(S - exact) <= 0.5 * ulp + exact * 2.0 ** -23)
+
+
+# ---------------------------------------------------------------------------
+# Brute force: every code is the grid point nearest to w (round-to-nearest).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("folded", [False, True])
+def test_codes_are_nearest_grid_points(bits, asym, folded):
+    rng = np.random.default_rng(100 + bits + 2 * asym + 4 * folded)
+    N, K = 5, 384
+    W = _random_groups(rng, N, K)
+    s = (rng.random(K).astype(np.float32) * 3 + 0.25) if folded else None
+    q = O.quantize(W, bits, 128, asym, s)
+    w = O.fold_act_scale(W, s).astype(np.float64)
+    S = np.repeat(q.scales.astype(np.float64), 128, axis=1)
+    Z = np.repeat(q.zeros.astype(np.float64), 128, axis=1) if asym else 2.0 ** (bits - 1)
+    Z = np.broadcast_to(Z, w.shape)
+    cand = np.arange(2 ** bits, dtype=np.float64)
+    grid = (cand[None, None, :] - Z[..., None]) * S[..., None]          # [N,K,codes]
+    dist = np.abs(w[..., None] - grid)
+    best = dist.min(axis=2)
+    got = np.take_along_axis(dist, q.codes[..., None].astype(np.int64), axis=2)[..., 0]
+    # the fp32 division can only move a decision when w/S is within one
+    # binary32 rounding of a half-integer
+    slack = np.abs(w) * 2.0 ** -22
+    assert np.all(got <= best + slack)
+    # exact ties (two grid points equally near) go to the even integer q = u - Z
+    ties = np.sum(dist == best[..., None], axis=2) > 1
+    if ties.any():
+        assert np.all(((q.codes.astype(np.int64) - Z.astype(np.int64))[ties] % 2) == 0)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_exact_ties_round_half_to_even(bits):
+    # S is a power of two when absmax = qmax * 2^-6; values (j + 1/2) S are ties.
+    qmax = 2 ** (bits - 1) - 1
+    S = 2.0 ** -6
+    vals = [qmax * S] + [(j + 0.5) * S for j in range(-qmax, qmax - 1)]
+    vals += [0.0] * (128 - len(vals))
+    W = np.array([vals], dtype=np.float16)
+    assert np.all(W.astype(np.float64) == np.array([vals]))
+    q = O.quantize(W, bits, 128, asymmetric=False)
+    assert float(q.scales[0, 0]) == S
+    signed = q.codes[0].astype(int) - 2 ** (bits - 1)
+    for j, v in enumerate(vals[1:1 + 2 * qmax - 1], start=1):
+        lo = int(np.floor(v / S))
+        expect = lo if lo % 2 == 0 else lo + 1
+        assert signed[j] == expect
+
+
+# ---------------------------------------------------------------------------
+# Range, clipping and the dequantization error bound.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("asym", [False, True])
+def test_codes_in_range_and_extremes_on_end_codes(bits, asym):
+    rng = np.random.default_rng(7 * bits + asym)
+    W = _random_groups(rng, 16, 1024)
+    q = O.quantize(W, bits, 128, asym)
+    assert q.codes.min() >= 0 and q.codes.max() <= 2 ** bits - 1
+    g = W.astype(np.float64).reshape(16, 8, 128)
+    c = q.codes.reshape(16, 8, 128).astype(int)
+    if asym:
+        # the group minimum lands on code 0, the maximum within one of the top
+        assert np.all(np.take_along_axis(c, g.argmin(2)[..., None], 2) == 0)
+        assert np.all(np.take_along_axis(c, g.argmax(2)[..., None], 2) >= 2 ** bits - 2)
+    else:
+        qmax = 2 ** (bits - 1) - 1
+        top = np.take_along_axis(c, np.abs(g).argmax(2)[..., None], 2)[..., 0] - 2 ** (bits - 1)
+        assert np.all(np.abs(top) == qmax)
+        assert c.min() >= 1  # -2^(b-1) is never produced by absmax scaling
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("folded", [False, True])
+def test_dequant_error_bound(bits, asym, folded):
+    rng = np.random.default_rng(31 + bits + 2 * asym + 4 * folded)
+    N, K = 32, 1024
+    W = _random_groups(rng, N, K)
+    s = (rng.random(K).astype(np.float32) * 3 + 0.25) if folded else None
+    q = O.quantize(W, bits, 128, asym, s)
+    w = O.fold_act_scale(W, s).astype(np.float64)
+    err = np.abs(w - O.dequantize(q))
+    S = np.repeat(q.scales.astype(np.float64), 128, axis=1)
+    if asym:
+        bound = S * (0.5 + (2 ** bits - 1) * 2.0 ** -11 + 2.0 ** -20)
+    else:
+        bound = S * (0.5 + 2.0 ** -20)
+    assert np.all(err <= bound)
+
+
+def test_group_size_trend():
+    # "Quantising ...", section "Post-training methods for 4-bit weights": a
+    # N(0, 0.02) row of 4096 with two 0.8 outliers; smaller groups reduce the
+    # mean absolute error (the page prints no values, only the trend).
+    rng = np.random.default_rng(0)
+    row = rng.normal(0, 0.02, 4096)
+    row[[10, 500]] = 0.8
+    W = row.astype(np.float16)[None, :]
+    errs = []
+    for G in (4096, 128, 32):
+        q = O.quantize(W, 4, G, asymmetric=False)
+        errs.append(np.abs(O.dequantize(q) - W.astype(np.float64)).mean())
+    assert errs[0] > errs[1] > errs[2]
+    assert errs[0] > 3 * errs[1]
+
+
+# ---------------------------------------------------------------------------
+# Degenerate groups.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_zero_group(bits):
+    W = np.zeros((2, 256), np.float16)
+    W[1, 128:] = _f16(np.linspace(-0.1, 0.1, 128))
+    qs = O.quantize(W, bits, 128, asymmetric=False)
+    assert float(qs.scales[0, 0]) == 0.0 and np.all(qs.codes[0] == 2 ** (bits - 1))
+    assert np.all(O.dequantize(qs)[0] == 0)
+    qa = O.quantize(W, bits, 128, asymmetric=True)
+    # zero range -> range 1 ("CMU 11-868 L19-L20", section "absmax and zero-point")
+    assert float(qa.scales[0, 0]) == float(np.float16(np.float32(1) / np.float32(2 ** bits - 1)))
+    assert float(qa.zeros[0, 0]) == 0 and np.all(qa.codes[0, :128] == 0)
+    assert np.all(O.dequantize(qa)[0, :128] == 0)
+
+
+@pytest.mark.parametrize("c", [0.3, -0.3, 0.01, 2.0])
+def test_constant_group_asymmetric(c):
+    bits = 4
+    W = np.full((1, 128), c, np.float16)
+    q = O.quantize(W, bits, 128, asymmetric=True)
+    S = float(np.float16(np.float32(1) / np.float32(15)))
+    assert float(q.scales[0, 0]) == S
+    cv = float(W[0, 0])
+    Z = min(max(round(Fraction(-cv) / Fraction(S)), 0), 15)
+    u = min(max(round(Fraction(cv) / Fraction(S)) + Z, 0), 15)
+    assert float(q.zeros[0, 0]) == Z and np.all(q.codes == u)
+
+
+def test_underflowing_scale():
+    # absmax below 7 * 2^-25: the fp16 scale rounds to 0
+    W = np.zeros((1, 128), np.float16)
+    W[0, 3] = np.float16(2.0 ** -24)
+    W[0, 9] = -np.float16(2.0 ** -24)
+    qs = O.quantize(W, 4, 128, asymmetric=False)
+    assert float(qs.scales[0, 0]) == 0 and np.all(qs.codes == 8)
+    qa = O.quantize(W, 4, 128, asymmetric=True)
+    assert float(qa.scales[0, 0]) == 0 and float(qa.zeros[0, 0]) == 0 and np.all(qa.codes == 0)
+
+
+# ---------------------------------------------------------------------------
+# Packed layout v1.
+# ---------------------------------------------------------------------------
+
+def test_layout_v1_fixed_words():
+    g = _load("layout_v1_words.json")
+    u4 = (np.arange(16) % 16).astype(np.uint8)[None, :]
+    w4 = O.pack_v1(u4, 4).view("<u4")[0].tolist()
+    assert w4 == [int(h, 16) for h in g["four_bit"]["words_hex"]]
+    u3 = (np.arange(32) % 8).astype(np.uint8)[None, :]
+    w3 = O.pack_v1(u3, 3).view("<u4")[0].tolist()
+    assert w3 == [int(h, 16) for h in g["three_bit"]["words_hex"]]
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_layout_v1_round_trip_and_single_code(bits):
+    rng = np.random.default_rng(bits)
+    u = rng.integers(0, 2 ** bits, size=(7, 256), dtype=np.uint8)
+    p = O.pack_v1(u, bits)
+    assert p.shape == (7, 256 * bits // 8)
+    assert np.array_equal(O.unpack_v1(p, bits, 256), u)
+    # a lone code lands on exactly the bits the definition names
+    for k in (0, 1, 2, 7, 13, 31, 200, 255):
+        one = np.zeros((1, 256), np.uint8)
+        one[0, k] = 2 ** bits - 1
+        words = O.pack_v1(one, bits).view("<u4")[0]
+        if bits == 4:
+            j, r = divmod(k, 8)
+            t, h = divmod(r, 2)
+            expect = {j: 0xF << (16 * h + 4 * t)}
+        else:
+            j, i = divmod(k, 32)
+            t, h = divmod(i, 2)
+            expect = {3 * j + t // 8: 3 << (16 * h + 2 * (t % 8)), 3 * j + 2: 1 << (16 * h + t)}
+        nz = {int(i): int(v) for i, v in enumerate(words) if v}
+        assert nz == expect
+
+
+# ---------------------------------------------------------------------------
+# Dequantization and the GEMV/GEMM against exact rational arithmetic.
+# ---------------------------------------------------------------------------
+
+def test_dequant_exact():
+    rng = np.random.default_rng(3)
+    W = _random_groups(rng, 3, 256)
+    q = O.quantize(W, 4, 128, asymmetric=True)
+    w_hat = O.dequantize(q)
+    for n in range(3):
+        for k in range(0, 256, 17):
+            g = k // 128
+            ref = (Fraction(int(q.codes[n, k])) - Fraction(float(q.zeros[n, g]))) * Fraction(float(q.scales[n, g]))
+            assert Fraction(float(w_hat[n, k])) == ref
+
+
+@pytest.mark.parametrize("with_scale", [False, True])
+def test_gemm_against_fractions(with_scale):
+    rng = np.random.default_rng(17)
+    M, N, K = 2, 3, 256
+    W = _random_groups(rng, N, K)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    s = (rng.random(K).astype(np.float32) + 0.5) if with_scale else None
+    q = O.quantize(W, 4, 128, asymmetric=True, act_scale=s)
+    Y = O.gemm(X.astype(np.float64), O.dequantize(q), s)
+    assert Y.shape == (M, N)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                g = k // 128
+                wk = (Fraction(int(q.codes[n, k])) - Fraction(float(q.zeros[n, g]))) * Fraction(float(q.scales[n, g]))
+                xk = Fraction(float(X[m, k]))
+                if s is not None:
+                    xk /= Fraction(float(s[k]))
+                acc += xk * wk
+            assert abs(float(Y[m, n]) - float(acc)) <= 1e-12 * max(1.0, abs(float(acc)))
+
+
+def test_gemm_constant_codes_closed_form():
+    # constant u, S, Z -> y_m = S (u - Z) sum_k x_mk
+    K = 512
+    q = O.Quantized(np.full((4, K), 11, np.uint8), np.full((4, K // 128), 0.0625, np.float16),
+                    np.full((4, K // 128), 3, np.float16), 4, 128, True)
+    X = np.random.default_rng(2).standard_normal((3, K)).astype(np.float16).astype(np.float64)
+    Y = O.gemm(X, O.dequantize(q))
+    assert np.allclose(Y, (0.0625 * 8 * X.sum(1))[:, None] * np.ones((1, 4)), rtol=1e-14, atol=0)
+
+
+def test_bf16_bits_exact():
+    bits = np.array([0x3F80, 0xC000, 0x4049, 0x0000, 0x8000, 0x7F7F], np.uint16)
+    vals = O.bf16_bits_to_f64(bits)
+    assert vals[0] == 1.0 and vals[1] == -2.0 and vals[3] == 0.0
+    assert vals[2] == 3.140625
+    assert vals[5] == 255 * 2.0 ** 120   # exponent 254, mantissa 127/128
+
+
+# ---------------------------------------------------------------------------
+# The AWQ fold.
+# ---------------------------------------------------------------------------
+
+def test_awq_fold_identity_without_quantization():
+    # (X diag(s)^-1)(diag(s) W) = X W ("Quantising ...", section "Why LLMs are
+    # hard to quantise"), to fp64 rounding, with quantization bypassed.
+    rng = np.random.default_rng(4)
+    W = _random_groups(rng, 8, 256)
+    X = rng.standard_normal((3, 256)).astype(np.float16)
+    s = rng.random(256).astype(np.float32) * 4 + 0.1
+    Wf = O.fold_act_scale(W, s).astype(np.float64)
+    Y = O.gemm(X.astype(np.float64), Wf, s)
+    Yref = X.astype(np.float64) @ W.astype(np.float64).T
+    assert O.rel_l2(Y, Yref) < 1e-6
+
+
+def test_awq_scaling_a_non_max_channel_shrinks_its_error():
+    # Lab 4 Question 2 of "MIT 6.5940 Lab 4 + Lab 5": scaling a salient channel
+    # by s while the group max stays put divides that weight's error by ~s.
+    rng = np.random.default_rng(9)
+    e1s, e2s = [], []
+    for trial in range(50):
+        w = (rng.standard_normal(128) * 0.02).astype(np.float16)
+        w[0] = np.float16(0.1)            # the group max, unchanged by scaling
+        j = 5
+        w[j] = np.float16(0.013 + 0.0005 * trial)
+        W = w[None, :]
+        s = np.ones(128, np.float32)
+        s[j] = 2.0
+        q1 = O.quantize(W, 3, 128, asymmetric=False)
+        q2 = O.quantize(W, 3, 128, asymmetric=False, act_scale=s)
+        assert q1.scales[0, 0] == q2.scales[0, 0]
+        S = float(q1.scales[0, 0])
+        e2 = abs(O.dequantize(q2)[0, j] / 2.0 - float(w[j]))
+        assert e2 <= S / 4 * (1 + 1e-6)
+        e1s.append(abs(O.dequantize(q1)[0, j] - float(w[j])))
+        e2s.append(e2)
+    # on average the error roughly halves (about S/4 unscaled, S/8 scaled)
+    assert np.mean(e2s) < 0.75 * np.mean(e1s)

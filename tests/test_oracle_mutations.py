@@ -1,0 +1,88 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a private copy of the oracle's source (a
+dropped term, a wrong sign, a wrong constant, swapped indices, a transposed
+operand), loads that copy as a separate module, and checks that at least one
+pin of ``test_oracle.py`` fails against it.  The real oracle is untouched.
+"""
+import importlib.util
+import inspect
+import os
+import sys
+import types
+
+import pytest
+
+import tests.test_oracle as pins
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "woq_oracle.py")
+
+MUTATIONS = {
+    "rint_to_floor": ("q = np.rint(np.divide(g, S32, dtype=np.float32))",
+                      "q = np.floor(np.divide(g, S32, dtype=np.float32))"),
+    "qmax_off_by_one": ("qmax = np.float32(half - 1)", "qmax = np.float32(half)"),
+    "asym_range_levels": ("qu = np.float32(2 ** bits - 1)", "qu = np.float32(2 ** bits)"),
+    "zero_point_sign": ("Zf = np.rint(np.divide(-mn, S32, dtype=np.float32))",
+                        "Zf = np.rint(np.divide(mn, S32, dtype=np.float32))"),
+    "zero_point_dropped": ("u = np.clip(q + Zf[:, :, None], 0, qu)", "u = np.clip(q, 0, qu)"),
+    "sym_bias_dropped": ("u = (q + half).astype(np.uint8)", "u = (q + half - 1).astype(np.uint8)"),
+    "zero_range_rule_dropped": ("r = np.where(r == 0, np.float32(1), r)", "r = r"),
+    "pack_nibble_order": ("<< np.uint32(16 * h + 4 * t)\n", "<< np.uint32(8 * h + 4 * t)\n"),
+    "pack3_high_bit": ("words[:, j, 2] |= ((u >> 2) & 1) << np.uint32(16 * h + t)",
+                       "words[:, j, 2] |= ((u >> 2) & 1) << np.uint32(16 * (1 - h) + t)"),
+    "dequant_zero_dropped": ("return (q.codes.astype(np.float64) - Z) * S",
+                             "return q.codes.astype(np.float64) * S"),
+    "gemm_transposed": ("return X64 @ np.asarray(w_hat, dtype=np.float64).T",
+                        "return (np.asarray(w_hat, dtype=np.float64) @ X64.T).T[:, ::-1]"),
+    "gemm_scale_multiplied": ("X64 = X64 / np.asarray(act_scale", "X64 = X64 * np.asarray(act_scale"),
+    "fold_divides": ("return np.multiply(w, s[None, :], dtype=np.float32)",
+                     "return np.divide(w, s[None, :], dtype=np.float32)"),
+    "scale_not_fp16": ("S = np.divide(a, qmax, dtype=np.float32).astype(np.float16)",
+                       "S = np.divide(a, qmax, dtype=np.float32).astype(np.float16) * np.float16(1.0009765625)"),
+}
+
+
+def _mutant(name, old, new):
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) >= 1, f"mutation {name}: pattern not found"
+    src = src.replace(old, new)
+    modname = f"woq_oracle_mutant_{name}"
+    mod = types.ModuleType(modname)
+    sys.modules[modname] = mod  # dataclasses look the module up by name
+    try:
+        exec(compile(src, f"<mutant {name}>", "exec"), mod.__dict__)
+    finally:
+        del sys.modules[modname]
+    return mod
+
+
+def _pin_calls():
+    """Every pin in test_oracle.py with each of its parameter combinations."""
+    calls = []
+    for fname, fn in inspect.getmembers(pins, inspect.isfunction):
+        if not fname.startswith("test_"):
+            continue
+        marks = getattr(fn, "pytestmark", [])
+        combos = [{}]
+        for m in marks:
+            if m.name != "parametrize":
+                continue
+            argname, values = m.args[0], m.args[1]
+            combos = [dict(c, **{argname: v}) for c in combos for v in values]
+        for c in combos:
+            calls.append((fname, fn, c))
+    return calls
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    old, new = MUTATIONS[name]
+    mutant = _mutant(name, old, new)
+    monkeypatch.setattr(pins, "O", mutant)
+    failed = []
+    for fname, fn, kwargs in _pin_calls():
+        try:
+            fn(**kwargs)
+        except Exception:  # an assertion or a crash: the pin rejects the mutant
+            failed.append(fname)
+    assert failed, f"no pin caught mutation {name}"

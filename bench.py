@@ -1,0 +1,262 @@
+"""Benchmark of the W4A16 g128 decode GEMV (M=1, K=N=8192) on one MI355X.
+
+One step = one pass of the whole path over the decode workload: quantize_pack
+of the fp16 weight matrix (fold, group statistics, scale / zero, codes,
+packing) followed by the fused dequantize-GEMV of a previously packed set.
+Inputs are resident in HBM before the timed region.  Weight copies and packed
+sets are rotated so that every launch streams from HBM rather than from the
+256 MB Infinity Cache.
+
+`value` is the GEMV's effective HBM bandwidth: algorithmic bytes (packed codes
++ fp16 scales + fp16 zeros + x + y) divided by the GEMV kernel's average
+duration, timed with HIP events recorded on the launch stream around each
+GEMV inside the timed steps.  The CPU oracle is timed on a bounded sample of
+the same workload (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--variants] [--extra FILE]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
+MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA (no sparsity)
+MALL_BYTES = 256 << 20
+METRIC = "W4A16 g128 GEMV µs + effective HBM GB/s (% peak) at M=1, K=N=8192"
+
+
+def gemv_bytes(N, K, bits, G, asym, M=1, act_scale=False):
+    """Algorithmic bytes of one dequant-GEMV/GEMM launch."""
+    b = N * K * bits // 8 + N * (K // G) * 2 * (1 + int(asym)) + M * K * 2 + M * N * 2
+    return b + (4 * K if act_scale else 0)
+
+
+def quantize_pack_bytes(N, K, bits, G, asym):
+    return N * K * 2 + N * K * bits // 8 + N * (K // G) * 2 * (1 + int(asym))
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--variants", action="store_true", help="also time 4/3-bit x sym/asym GEMV variants")
+    p.add_argument("--extra", default=None, help="write per-config results (JSON lines) to this file")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events recorded on the current (launch) stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+
+
+def rotate_count(bytes_per_set, minimum=4):
+    return max(minimum, int(np.ceil(2 * MALL_BYTES / bytes_per_set)) + 1)
+
+
+def time_gemv_variant(torch, ops, synth, lin, bits, asym, iters=100):
+    """Average GEMV kernel duration (ms) over rotated packed sets."""
+    N, K, G = lin.N, lin.K, 128
+    W = torch.from_numpy(lin.W).cuda()
+    x = torch.from_numpy(lin.X[0]).cuda()
+    nb = gemv_bytes(N, K, bits, G, asym)
+    R = rotate_count(nb)
+    sets = [ops.quantize_pack(W, bits, G, asym) for _ in range(R)]
+    y = torch.empty(N, dtype=torch.float16, device="cuda")
+    for i in range(10):
+        ops.gemv(x, *sets[i % R], N, K, bits, G, out=y)
+    t = Timer(torch)
+    for i in range(iters):
+        e = t.start()
+        ops.gemv(x, *sets[i % R], N, K, bits, G, out=y)
+        t.stop(e)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    del sets
+    return ms, nb
+
+
+def cpu_baseline(lin, packed_gpu, bits, G, asym, y_gpu):
+    """Time the oracle (as it stands) on the host: unpack + dequantize + fp64
+    GEMV of the whole decode workload, single-threaded BLAS."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import woq_oracle as O
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        ref_packed, ref_scales, ref_zeros, q = O.quantize_pack(lin.W, bits, G, asym)
+        t_quant = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        codes = O.unpack_v1(ref_packed, bits, lin.K)
+        qq = O.Quantized(codes, ref_scales, ref_zeros, bits, G, asym)
+        y_ref = O.gemm(lin.X.astype(np.float64), O.dequantize(qq))[0]
+        t_gemv = time.perf_counter() - t0
+    parity = {
+        "packed_equal": bool(np.array_equal(packed_gpu[0], ref_packed)),
+        "scales_equal": bool(np.array_equal(packed_gpu[1].view(np.uint16), ref_scales.view(np.uint16))),
+        "zeros_equal": bool(ref_zeros is None or np.array_equal(packed_gpu[2].view(np.uint16),
+                                                                ref_zeros.view(np.uint16))),
+        "gemv_rel_l2": O.rel_l2(y_gpu, y_ref),
+    }
+    nb = gemv_bytes(lin.N, lin.K, bits, G, asym)
+    base = {
+        "value": nb / t_gemv / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"one full M=1 K=N={lin.K} GEMV from the packed weights (unpack + dequantize + fp64 matvec, "
+                   f"{t_gemv:.2f} s) and one full quantize_pack ({t_quant:.2f} s); numpy, BLAS limited to 1 thread"),
+        "gemv_s": t_gemv,
+        "quantize_pack_s": t_quant,
+    }
+    return base, parity
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is not sharded "
+              "across GPUs in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from weight_only_quantization_quantize_amd import _lib, ops, synth
+
+    _lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bits, G, asym = 4, 128, True
+    lin = synth.c2_decode()
+    N, K = lin.N, lin.K
+
+    # Resident inputs: rotated fp16 weight copies and packed sets.
+    W0 = torch.from_numpy(lin.W).to(dev)
+    nW = 4  # 4 x 134 MB > 2 x MALL
+    Ws = [W0] + [W0.clone() for _ in range(nW - 1)]
+    x = torch.from_numpy(lin.X[0]).to(dev)
+    nb = gemv_bytes(N, K, bits, G, asym)
+    R = rotate_count(nb)
+    sets = [ops.quantize_pack(W0, bits, G, asym) for _ in range(R)]
+    y = torch.empty(N, dtype=torch.float16, device=dev)
+    torch.cuda.synchronize()
+
+    tq, tg = Timer(torch), Timer(torch)
+
+    def step(i, timed):
+        dst = sets[i % R]
+        src = sets[(i + R // 2) % R]
+        if timed:
+            e = tq.start()
+        ops.quantize_pack(Ws[i % nW], bits, G, asym, None, out=dst)
+        if timed:
+            tq.stop(e)
+            e = tg.start()
+        ops.gemv(x, *src, N, K, bits, G, out=y)
+        if timed:
+            tg.stop(e)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev0.elapsed_time(ev1)
+    gemv_ms = tg.mean_ms()
+    qp_ms = tq.mean_ms()
+
+    achieved = nb / (gemv_ms * 1e-3) / 1e9
+    qp_nb = quantize_pack_bytes(N, K, bits, G, asym)
+    result = {
+        "metric": METRIC,
+        "value": round(achieved, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode GEMV M=1 K=8192 N=8192, 4-bit asymmetric zero-point RTN, group 128, fp16 "
+                        "activations, fp32 accumulate; weights N(0,0.02) with 0.1% N(0,0.5) outliers",
+            "M": 1, "K": K, "N": N, "bits": bits, "group_size": G, "asymmetric": asym,
+            "rotated_sets": R, "step": "quantize_pack + gemv",
+        },
+        "gemv_us": round(gemv_ms * 1e3, 3),
+        "gemv_pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "quantize_pack_us": round(qp_ms * 1e3, 2),
+        "quantize_pack_gbs": round(qp_nb / (qp_ms * 1e-3) / 1e9, 1),
+        "wall_s": round(wall, 3),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gemv_kernel<4-bit, asymmetric, f16>",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": nb,
+        },
+    }
+
+    if args.variants:
+        var = {}
+        for b_, a_ in [(4, True), (4, False), (3, True), (3, False)]:
+            ms, vb = time_gemv_variant(torch, ops, synth, lin, b_, a_)
+            var[f"{b_}bit_{'asym' if a_ else 'sym'}"] = {
+                "gemv_us": round(ms * 1e3, 3), "gbs": round(vb / (ms * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * vb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2), "bytes": vb}
+        result["variants"] = var
+
+    if not args.no_cpu_baseline:
+        ops.gemv(x, *sets[0], N, K, bits, G, out=y)
+        torch.cuda.synchronize()
+        host_sets = (sets[0][0].cpu().numpy(), sets[0][1].cpu().numpy(), sets[0][2].cpu().numpy())
+        base, parity = cpu_baseline(lin, host_sets, bits, G, asym, y.cpu().numpy().astype(np.float64))
+        result["cpu_baseline"] = base
+        result["parity"] = parity
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * woq.h -- C ABI of libwoq: group-wise weight-only 3/4-bit quantization and
+ * the fused dequantize + GEMV/GEMM that consumes it, for AMD MI355X (gfx950).
+ *
+ * What is computed (the pages this library implements):
+ *
+ *  - Group-wise round-to-nearest quantization of a weight row, one scale (and
+ *    zero point) per group of consecutive weights along K ("Quantising Large
+ *    Language Models for Efficient Inference", section "Post-training methods
+ *    for 4-bit weights"); symmetric absmax and asymmetric zero-point forms
+ *    ("CMU 11-868 L19-L20 Model Quantization", section "absmax and
+ *    zero-point"; "LLM Quantization: 160GB Model on a Laptop", sections
+ *    "Symmetric Quantization" and "Asymmetric Quantization"); AutoGPTQ-style
+ *    parameters bits and group_size ("CMU 11-868 ...", section "Setup and
+ *    results").
+ *  - An optional per-input-channel AWQ scale s: weights are multiplied by s
+ *    before quantization and activations divided by s in the matmul
+ *    ("Quantising ...", section "Why LLMs are hard to quantise":
+ *    Y = (X diag(s)^-1)(diag(s) W); "MIT 6.5940 Lab 4 + Lab 5", Lab 4
+ *    Question 2).
+ *  - A W4A16 matmul whose weights are dequantized on the fly inside the
+ *    kernel ("Quantising ...", section "Weight-only vs weight-and-activation
+ *    quantisation"), with fp16 or bf16 activations and fp32 accumulation.
+ *
+ * Quantization of one group of G weights w (fp32 after the optional fold
+ * w = fl32(W * s[k]); every step one correctly rounded binary32 operation,
+ * rne = round half to even, f16() = binary16 round-to-nearest-even):
+ *
+ *   symmetric : S = f16(max|w| / (2^(b-1)-1));
+ *               u = clip(rne(w / S), -2^(b-1), 2^(b-1)-1) + 2^(b-1);
+ *               S == 0 -> u = 2^(b-1).  zeros are implied (2^(b-1)).
+ *   asymmetric: r = max - min, r := 1 if r == 0;  S = f16(r / (2^b-1));
+ *               Z = clip(rne(-min / S), 0, 2^b-1);
+ *               u = clip(rne(w / S) + Z, 0, 2^b-1);  S == 0 -> Z = u = 0.
+ *   dequantized weight: w_hat = (u - Z) * S.
+ *
+ * Packed layout v1 (WOQ_LAYOUT_V1).  Rows n = 0..N-1 back to back, each
+ * K*bits/8 bytes; groups are contiguous along K starting at k = 0.  Words are
+ * little-endian 32-bit.
+ *   4-bit: word j of a row holds k in [8j, 8j+8); the code of
+ *          k = 8j + 2t + h (t = 0..3, h = 0..1) is at bits [16h+4t, 16h+4t+4).
+ *          (w >> 4t) & 0x000F000F therefore yields the pair (k, k+1) in the
+ *          two 16-bit halves of a register.
+ *   3-bit: a 12-byte unit j (words w0, w1, w2) holds k in [32j, 32j+32); for
+ *          i = k - 32j = 2t + h (t = 0..15, h = 0..1) the low two bits of the
+ *          code are in w_(t/8) at bits [16h + 2(t%8), +2) and the high bit in
+ *          w2 at bit 16h + t.
+ *   scales: fp16 [N, K/G] row-major.  zeros: fp16 [N, K/G] row-major holding
+ *          the integer Z (asymmetric only).
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller (the library
+ *    never allocates, frees or synchronizes).  act_scale may be NULL.
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream); all
+ *    work is enqueued asynchronously on it.  Errors detected before launch are
+ *    returned; faults during execution surface at the caller's next sync.
+ *  - Arguments are validated before any HIP call.  Invalid arguments return
+ *    WOQ_ERR_INVALID_ARGUMENT, valid but unimplemented combinations
+ *    WOQ_ERR_UNSUPPORTED, a failing HIP launch WOQ_ERR_HIP.  woq_last_error()
+ *    gives a thread-local message for the last failing call on this thread.
+ *  - Constraints: bits in {3, 4}; group_size % 32 == 0; K % group_size == 0;
+ *    N >= 1, K >= 32, M >= 1; packed, X/x and Y/y 16-byte aligned; scales and
+ *    zeros 2-byte aligned; zeros != NULL exactly when asymmetric != 0.
+ *  - Inputs must be finite.  Weights whose fp16 scale would overflow give
+ *    unspecified results.  No C++ exception crosses this boundary.
+ *  - Calls are thread-safe; the library keeps no state besides a cached
+ *    device-property query and the per-thread error message.
+ */
+#ifndef WOQ_H_
+#define WOQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WOQ_LAYOUT_V1 1
+
+typedef enum woq_status {
+  WOQ_OK = 0,
+  WOQ_ERR_INVALID_ARGUMENT = 1,
+  WOQ_ERR_UNSUPPORTED = 2,
+  WOQ_ERR_HIP = 3,
+  WOQ_ERR_INTERNAL = 4
+} woq_status;
+
+/* Activation / output element type. */
+typedef enum woq_dtype { WOQ_F16 = 0, WOQ_BF16 = 1 } woq_dtype;
+
+/* Layout version produced and consumed by this library (WOQ_LAYOUT_V1). */
+int32_t woq_layout_version(void);
+
+/* Bytes of the packed code array for an [N, K] matrix: N * K * bits / 8.
+ * Returns 0 for invalid arguments. */
+size_t woq_packed_bytes(int64_t N, int64_t K, int32_t bits);
+
+/* Bytes of one scale (or zero) array: N * (K / group_size) * 2.
+ * Returns 0 for invalid arguments. */
+size_t woq_scales_bytes(int64_t N, int64_t K, int32_t group_size);
+
+/* Workspace bytes woq_w4a16_gemv / woq_w4a16_gemm need for this shape
+ * (currently always 0: every kernel reduces in registers and LDS).  Callers
+ * may pass workspace = NULL when this returns 0. */
+size_t woq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size);
+
+/* Quantize fp16 weights W [N, K] (row-major, output channel n, input channel
+ * k) group-wise and write the packed codes, scales and zeros.
+ *   W         : fp16 [N, K]
+ *   act_scale : fp32 [K] AWQ scale s multiplied into column k before the
+ *               group statistics, or NULL
+ *   packed    : out, uint8 [N, K*bits/8] in layout v1
+ *   scales    : out, fp16 [N, K/group_size]
+ *   zeros     : out, fp16 [N, K/group_size] when asymmetric, else NULL
+ * Bit-exact with the definition above (IEEE division, RNE everywhere). */
+woq_status woq_quantize_pack(const void* W, const float* act_scale, int64_t N, int64_t K,
+                             int32_t bits, int32_t group_size, int32_t asymmetric,
+                             void* packed, void* scales, void* zeros, void* stream);
+
+/* y[n] = sum_k (x[k] / s[k]) * w_hat[n, k]  (M = 1 decode GEMV).
+ *   x         : [K] of xdtype (WOQ_F16 or WOQ_BF16)
+ *   act_scale : fp32 [K] (the same s given to woq_quantize_pack) or NULL
+ *   packed, scales, zeros : as written by woq_quantize_pack
+ *   y         : out, [N] of xdtype
+ * Accumulates in fp32.  x / s is rounded once to xdtype before use; the
+ * integer (u - Z) is multiplied exactly and S is applied in fp32 per group. */
+woq_status woq_w4a16_gemv(const void* x, int32_t xdtype, const float* act_scale,
+                          const void* packed, const void* scales, const void* zeros,
+                          int64_t N, int64_t K, int32_t bits, int32_t group_size, int32_t asymmetric,
+                          void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Y[m, n] = sum_k (X[m, k] / s[k]) * w_hat[n, k]  for M >= 1.
+ *   X : [M, K] row-major of xdtype;  Y : out, [M, N] row-major of xdtype.
+ * Small M decodes weights in registers and feeds MFMA with an exact integer
+ * (u - Z) and per-group fp32 scaling; large M stages dequantized tiles
+ * (rounded to xdtype) in LDS for MFMA.  fp32 accumulation throughout. */
+woq_status woq_w4a16_gemm(const void* X, int32_t xdtype, const float* act_scale,
+                          const void* packed, const void* scales, const void* zeros,
+                          int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size,
+                          int32_t asymmetric, void* Y, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Test aid: w_hat = (u - Z) * S as fp32 [N, K] (exact: |u - Z| < 16 and S has
+ * 11 significant bits).  Pseudo-quantization's dequantize step ("MIT 6.5940
+ * Lab 4 + Lab 5", Lab 4 setup). */
+woq_status woq_dequantize(const void* packed, const void* scales, const void* zeros,
+                          int64_t N, int64_t K, int32_t bits, int32_t group_size, int32_t asymmetric,
+                          float* out, void* stream);
+
+/* Static text for a status code. */
+const char* woq_status_string(woq_status status);
+
+/* Thread-local message describing the last failing call on this thread
+ * ("" if none).  Valid until the next library call on this thread. */
+const char* woq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WOQ_H_ */

@@ -166,7 +166,8 @@ def quantize(
     with np.errstate(divide="ignore", invalid="ignore"):
         Zf = np.rint(np.divide(-mn, S32, dtype=np.float32))
         Zf = np.where(S32 == 0, np.float32(0), Zf)
-        Zf = np.clip(Zf, 0, qu)
+        # Z is an integer; adding +0 stores an integer zero as +0, never -0
+        Zf = np.clip(Zf, 0, qu) + np.float32(0)
         q = np.rint(np.divide(g, S32[:, :, None], dtype=np.float32))
     q = np.where(S32[:, :, None] == 0, -Zf[:, :, None], q)
     u = np.clip(q + Zf[:, :, None], 0, qu).astype(np.uint8)

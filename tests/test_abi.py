@@ -1,0 +1,165 @@
+"""The C ABI of libwoq on the host: every declared symbol is exported, size
+queries are right, and every invalid argument is rejected before any HIP call.
+
+No test here launches a kernel: each call passes at least one invalid
+argument, so the library returns during validation.
+"""
+import os
+import re
+
+import pytest
+
+from weight_only_quantization_quantize_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "woq.h")
+
+FAKE = 0x10000  # an aligned address that is never dereferenced (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(woq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("woq_quantize_pack", "woq_w4a16_gemv", "woq_w4a16_gemm", "woq_packed_bytes", "woq_workspace_bytes",
+              "woq_status_string", "woq_last_error", "woq_dequantize", "woq_scales_bytes", "woq_layout_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_size_queries(lib):
+    assert lib.woq_layout_version() == 1
+    assert lib.woq_packed_bytes(8192, 8192, 4) == 8192 * 4096
+    assert lib.woq_packed_bytes(8192, 8192, 3) == 8192 * 3072
+    assert lib.woq_packed_bytes(4096, 11008, 3) == 4096 * 11008 * 3 // 8
+    assert lib.woq_packed_bytes(8192, 8192, 5) == 0
+    assert lib.woq_packed_bytes(8192, 100, 4) == 0
+    assert lib.woq_scales_bytes(8192, 8192, 128) == 8192 * 64 * 2
+    assert lib.woq_scales_bytes(8192, 8192, 100) == 0
+    assert lib.woq_workspace_bytes(1, 8192, 8192, 4, 128) == 0
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "WOQ_OK"), (1, "WOQ_ERR_INVALID_ARGUMENT"), (2, "WOQ_ERR_UNSUPPORTED"),
+                       (3, "WOQ_ERR_HIP"), (4, "WOQ_ERR_INTERNAL")]:
+        assert lib.woq_status_string(code).decode() == name
+
+
+def _qp(lib, **kw):
+    a = dict(W=FAKE, s=None, N=64, K=256, bits=4, G=128, asym=1, packed=FAKE, scales=FAKE, zeros=FAKE)
+    a.update(kw)
+    return lib.woq_quantize_pack(a["W"], a["s"], a["N"], a["K"], a["bits"], a["G"], a["asym"], a["packed"],
+                                 a["scales"], a["zeros"], None)
+
+
+@pytest.mark.parametrize(
+    "kw, needle",
+    [
+        (dict(bits=2), "bits"),
+        (dict(bits=8), "bits"),
+        (dict(N=0), "N must"),
+        (dict(K=0), "K must"),
+        (dict(K=100), "K must"),
+        (dict(G=0), "group_size"),
+        (dict(G=48), "group_size"),
+        (dict(K=384, G=256), "multiple of group_size"),
+        (dict(W=None), "W must"),
+        (dict(W=FAKE + 2), "W must be 16-byte"),
+        (dict(packed=None), "packed"),
+        (dict(packed=FAKE + 4), "packed must be 16-byte"),
+        (dict(scales=None), "scales"),
+        (dict(scales=FAKE + 1), "scales must be 2-byte"),
+        (dict(zeros=None), "zeros must not be NULL"),
+        (dict(asym=0), "zeros must be NULL"),
+        (dict(zeros=FAKE + 1), "zeros must be 2-byte"),
+        (dict(s=FAKE + 4), "act_scale"),
+    ],
+)
+def test_quantize_pack_rejects(lib, kw, needle):
+    assert _qp(lib, **kw) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    assert needle in lib.woq_last_error().decode()
+
+
+def _gemv(lib, **kw):
+    a = dict(x=FAKE, dt=0, s=None, packed=FAKE, scales=FAKE, zeros=FAKE, N=64, K=256, bits=4, G=128, asym=1,
+             y=FAKE)
+    a.update(kw)
+    return lib.woq_w4a16_gemv(a["x"], a["dt"], a["s"], a["packed"], a["scales"], a["zeros"], a["N"], a["K"],
+                              a["bits"], a["G"], a["asym"], a["y"], None, 0, None)
+
+
+@pytest.mark.parametrize(
+    "kw, needle",
+    [
+        (dict(dt=2), "xdtype"),
+        (dict(x=None), "x and y"),
+        (dict(y=None), "x and y"),
+        (dict(x=FAKE + 8), "x must be 16-byte"),
+        (dict(y=FAKE + 1), "y must be 2-byte"),
+        (dict(bits=5), "bits"),
+        (dict(K=96, G=64), "multiple of group_size"),
+        (dict(asym=0), "zeros must be NULL"),
+        (dict(s=FAKE + 8), "act_scale"),
+    ],
+)
+def test_gemv_rejects(lib, kw, needle):
+    assert _gemv(lib, **kw) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    assert needle in lib.woq_last_error().decode()
+
+
+def _gemm(lib, **kw):
+    a = dict(X=FAKE, dt=0, s=None, packed=FAKE, scales=FAKE, zeros=FAKE, M=4, N=64, K=256, bits=4, G=128, asym=1,
+             Y=FAKE)
+    a.update(kw)
+    return lib.woq_w4a16_gemm(a["X"], a["dt"], a["s"], a["packed"], a["scales"], a["zeros"], a["M"], a["N"], a["K"],
+                              a["bits"], a["G"], a["asym"], a["Y"], None, 0, None)
+
+
+@pytest.mark.parametrize(
+    "kw, needle",
+    [
+        (dict(M=0), "M must"),
+        (dict(dt=-1), "xdtype"),
+        (dict(X=None), "X and Y"),
+        (dict(X=FAKE + 2), "X must be 16-byte"),
+        (dict(Y=FAKE + 1), "Y must be 2-byte"),
+        (dict(N=-3), "N must"),
+        (dict(zeros=None), "zeros must not be NULL"),
+    ],
+)
+def test_gemm_rejects(lib, kw, needle):
+    assert _gemm(lib, **kw) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    assert needle in lib.woq_last_error().decode()
+
+
+def test_dequantize_rejects(lib):
+    st = lib.woq_dequantize(FAKE, FAKE, FAKE, 64, 256, 4, 128, 1, None, None)
+    assert st == _lib.WOQ_ERR_INVALID_ARGUMENT
+    st = lib.woq_dequantize(FAKE, FAKE, FAKE, 64, 256, 4, 128, 1, FAKE + 4, None)
+    assert st == _lib.WOQ_ERR_INVALID_ARGUMENT
+
+
+def test_oversized_shapes_are_unsupported(lib):
+    assert _gemv(lib, N=2 ** 31 + 64) == _lib.WOQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="only meaningful on a host without an AMD GPU")
+def test_hip_error_surfaces_without_a_device(lib):
+    # valid arguments on a host with no GPU: the launch fails inside HIP
+    st = _qp(lib)
+    assert st == _lib.WOQ_ERR_HIP
+    assert "quantize_pack launch" in lib.woq_last_error().decode()

@@ -1,0 +1,338 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Packed codes, scales and zeros must match the oracle byte for byte; GEMV /
+GEMM outputs must be within relative L2 2e-3 of the oracle's fp64 result on
+the same dequantized weights.  Shapes span several tiles with ragged tails;
+the full-size workloads are checked on sampled rows / columns that the
+oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import woq_oracle as O
+from weight_only_quantization_quantize_amd import ops, synth
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 2e-3
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def gpu_f16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16)).to(DEV)
+
+
+def gpu_x(a, xdtype):
+    if xdtype == "f16":
+        return gpu_f16(a)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def gpu_f32(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def host(t):
+    if t.dtype == torch.bfloat16:
+        return O.bf16_bits_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.cpu().numpy()
+
+
+def quantize_both(W, bits, G, asym, s=None):
+    packed, scales, zeros = ops.quantize_pack(gpu_f16(W), bits, G, asym, gpu_f32(s))
+    ref_packed, ref_scales, ref_zeros, q = O.quantize_pack(W, bits, G, asym, s)
+    return (packed, scales, zeros), (ref_packed, ref_scales, ref_zeros, q)
+
+
+def assert_pack_equal(gpu, ref):
+    packed, scales, zeros = gpu
+    ref_packed, ref_scales, ref_zeros, _ = ref
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), ref_packed), "packed codes differ"
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), ref_scales.view(np.uint16)), "scales differ"
+    if ref_zeros is None:
+        assert zeros is None
+    else:
+        assert np.array_equal(zeros.cpu().numpy().view(np.uint16), ref_zeros.view(np.uint16)), "zeros differ"
+
+
+# ---------------------------------------------------------------------------
+# quantize_pack: byte-equal
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("asym", [False, True])
+def test_quantize_pack_small_workload(bits, asym):
+    lin = synth.c1_small()
+    _say(f"quantize_pack c1 bits={bits} asym={asym}")
+    gpu, ref = quantize_both(lin.W, bits, 128, asym)
+    assert_pack_equal(gpu, ref)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("asym", [False, True])
+def test_quantize_pack_decode_shape(bits, asym):
+    lin = synth.c2_decode()
+    _say(f"quantize_pack c2 8192x8192 bits={bits} asym={asym}")
+    gpu, ref = quantize_both(lin.W, bits, 128, asym)
+    assert_pack_equal(gpu, ref)
+
+
+@pytest.mark.parametrize("i", [0, 4, 6])
+@pytest.mark.parametrize("bits", [3, 4])
+def test_quantize_pack_awq_fold(i, bits):
+    lin = synth.c3_linear(i)
+    _say(f"quantize_pack c3 {lin.name} bits={bits} with AWQ scale")
+    gpu, ref = quantize_both(lin.W, bits, 128, True, lin.act_scale)
+    assert_pack_equal(gpu, ref)
+
+
+@pytest.mark.parametrize("G", [32, 64, 256, 96, 4096])
+@pytest.mark.parametrize("asym", [False, True])
+def test_quantize_pack_group_sizes(G, asym):
+    rng = np.random.default_rng(G)
+    K = 4096 if G != 96 else 96 * 40
+    W = (rng.standard_normal((37, K)).astype(np.float32) * 0.02).astype(np.float16)
+    _say(f"quantize_pack G={G} K={K} asym={asym}")
+    for bits in (3, 4):
+        gpu, ref = quantize_both(W, bits, G, asym)
+        assert_pack_equal(gpu, ref)
+
+
+def adversarial_weights():
+    """Rows of 128-weight groups built to hit every branch of the definition."""
+    rows = []
+    z = np.zeros(256, np.float32)
+    rows.append(z.copy())                                         # all-zero groups
+    c = np.full(256, 0.3, np.float32); c[128:] = -0.02; rows.append(c)   # constant groups
+    t = np.zeros(256, np.float32)                                 # exact ties, S = 2^-6 (4-bit)
+    t[0] = 7 * 2.0 ** -6
+    t[1:15] = (np.arange(-7, 7) + 0.5) * 2.0 ** -6
+    t[128] = 3 * 2.0 ** -6                                        # 3-bit ties in group 2
+    t[129:135] = (np.arange(-3, 3) + 0.5) * 2.0 ** -6
+    rows.append(t)
+    u = np.zeros(256, np.float32); u[5] = 2.0 ** -24; u[9] = -2.0 ** -24; rows.append(u)   # underflowing S
+    p = np.abs(np.random.default_rng(1).standard_normal(256)).astype(np.float32) * 0.01 + 0.2
+    rows.append(p)                                                # all-positive groups (Z clipped at 0)
+    n = -p; rows.append(n)                                        # all-negative groups
+    big = np.random.default_rng(2).standard_normal(256).astype(np.float32) * 100.0; rows.append(big)
+    sub = np.random.default_rng(3).standard_normal(256).astype(np.float32) * 1e-6; rows.append(sub)  # subnormal S
+    return np.stack(rows).astype(np.float16)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("asym", [False, True])
+def test_quantize_pack_adversarial_groups(bits, asym):
+    W = adversarial_weights()
+    _say(f"quantize_pack adversarial bits={bits} asym={asym}")
+    gpu, ref = quantize_both(W, bits, 128, asym)
+    assert_pack_equal(gpu, ref)
+    s = np.linspace(0.5, 3.0, W.shape[1]).astype(np.float32)
+    gpu, ref = quantize_both(W, bits, 128, asym, s)
+    assert_pack_equal(gpu, ref)
+
+
+def test_quantize_pack_worked_example():
+    # "LLM Quantization: 160GB Model on a Laptop", section "Symmetric
+    # Quantization": codes [-7, 1, 1, -1, 1, -4]; zero padding to a 128 group.
+    W = np.zeros((1, 128), np.float16)
+    W[0, :6] = np.array([-0.89, 0.16, 0.08, -0.13, 0.16, -0.54], np.float32).astype(np.float16)
+    packed, scales, zeros = ops.quantize_pack(gpu_f16(W), 4, 128, False)
+    codes = O.unpack_v1(packed.cpu().numpy(), 4, 128)
+    assert (codes[0, :6].astype(int) - 8).tolist() == [-7, 1, 1, -1, 1, -4]
+    assert abs(float(scales.cpu().numpy()[0, 0]) - 0.127) < 5e-4
+
+
+def test_quantize_pack_leaves_memory_past_the_outputs_untouched():
+    lin = synth.c1_small()
+    N, K = lin.W.shape
+    guard = 4096
+    packed = torch.full((N * K // 2 + guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    scales = torch.full((N * K // 128 + guard,), 7.0, dtype=torch.float16, device=DEV)
+    zeros = torch.full((N * K // 128 + guard,), 7.0, dtype=torch.float16, device=DEV)
+    out = (packed[: N * K // 2].view(N, K // 2), scales[: N * K // 128].view(N, K // 128),
+           zeros[: N * K // 128].view(N, K // 128))
+    ops.quantize_pack(gpu_f16(lin.W), 4, 128, True, None, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(packed[N * K // 2:] == 0xA5)
+    assert torch.all(scales[N * K // 128:] == 7.0) and torch.all(zeros[N * K // 128:] == 7.0)
+
+
+# ---------------------------------------------------------------------------
+# dequantize and the layout decode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("asym", [False, True])
+def test_dequantize_exact(bits, asym):
+    lin = synth.c1_small()
+    gpu, ref = quantize_both(lin.W, bits, 128, asym)
+    w_hat = ops.dequantize(*gpu, 1024, 1024, bits, 128).cpu().numpy().astype(np.float64)
+    assert np.array_equal(w_hat, O.dequantize(ref[3]))
+
+
+# ---------------------------------------------------------------------------
+# GEMV
+# ---------------------------------------------------------------------------
+
+def gemv_case(lin, bits, asym, xdtype="f16", G=128, use_scale=True):
+    s = lin.act_scale if use_scale else None
+    gpu, ref = quantize_both(lin.W, bits, G, asym, s)
+    assert_pack_equal(gpu, ref)
+    X = lin.X if xdtype == "f16" else synth.to_bf16_bits(lin.X.astype(np.float32))
+    y = ops.gemv(gpu_x(X[0], xdtype), *gpu, lin.N, lin.K, bits, G, gpu_f32(s))
+    y_ref = O.gemm(O.activations_f64(X, xdtype), O.dequantize(ref[3]), s)[0]
+    err = O.rel_l2(host(y), y_ref)
+    _say(f"gemv {lin.name} bits={bits} asym={asym} {xdtype} G={G}: rel_l2={err:.2e}")
+    assert err <= REL_L2
+    return err
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("xdtype", ["f16", "bf16"])
+def test_gemv_small_workload(bits, asym, xdtype):
+    gemv_case(synth.c1_small(), bits, asym, xdtype)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("asym", [False, True])
+def test_gemv_decode_shape(bits, asym):
+    gemv_case(synth.c2_decode(), bits, asym)
+
+
+@pytest.mark.parametrize("i", range(7))
+@pytest.mark.parametrize("bits", [3, 4])
+def test_gemv_llama_linears_with_awq(i, bits):
+    gemv_case(synth.c3_linear(i), bits, True)
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (67, 160), (129, 640), (33, 2048 + 128), (250, 8192 + 512),
+                                 (17, 16384), (5, 20480)])
+def test_gemv_ragged_shapes(N, K):
+    rng = np.random.default_rng(N * 7 + K)
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    x = rng.standard_normal((1, K)).astype(np.float16)
+    G = 32 if K % 128 else 128
+    lin = synth.Linear(f"ragged_{N}x{K}", 1, N, K, W, x)
+    for bits in (3, 4):
+        gemv_case(lin, bits, True, G=G)
+
+
+@pytest.mark.parametrize("G", [32, 64, 256, 4096])
+def test_gemv_group_sizes(G):
+    lin = synth.c3_linear(0)
+    gemv_case(lin, 4, True, G=G)
+    gemv_case(lin, 3, False, G=G)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_gemv_one_hot_columns(bits):
+    # x = e_k isolates column k of w_hat: every layout position decodes right
+    lin = synth.c1_small()
+    gpu, ref = quantize_both(lin.W, bits, 128, True)
+    w_hat16 = O.dequantize(ref[3]).astype(np.float16)
+    for k in list(range(0, 40)) + [127, 128, 511, 1000, 1023]:
+        x = np.zeros(1024, np.float16)
+        x[k] = 1.0
+        y = ops.gemv(gpu_f16(x), *gpu, 1024, 1024, bits, 128).cpu().numpy()
+        assert np.array_equal(y.view(np.uint16), w_hat16[:, k].view(np.uint16)), f"column {k}"
+
+
+def test_gemv_is_deterministic():
+    lin = synth.c1_small()
+    gpu, _ = quantize_both(lin.W, 4, 128, True)
+    a = ops.gemv(gpu_f16(lin.X[0]), *gpu, 1024, 1024).cpu().numpy()
+    b = ops.gemv(gpu_f16(lin.X[0]), *gpu, 1024, 1024).cpu().numpy()
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+
+def gemm_case(W, X, xdtype, bits, asym, G=128, s=None, rows=None, label=""):
+    """X: fp16 values or bf16 bits [M, K].  rows: sampled output columns n the
+    oracle checks (all when None)."""
+    N, K = W.shape
+    M = X.shape[0]
+    packed, scales, zeros = ops.quantize_pack(gpu_f16(W), bits, G, asym, gpu_f32(s))
+    Y = ops.gemm(gpu_x(X, xdtype), packed, scales, zeros, N, K, bits, G, gpu_f32(s))
+    Yh = host(Y)
+    sel = np.arange(N) if rows is None else np.asarray(rows)
+    ref_packed, ref_scales, ref_zeros, q = O.quantize_pack(W[sel], bits, G, asym, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy()[sel], ref_packed)
+    assert np.array_equal(scales.cpu().numpy()[sel].view(np.uint16), ref_scales.view(np.uint16))
+    Y_ref = O.gemm(O.activations_f64(X, xdtype), O.dequantize(q), s)
+    err = O.rel_l2(Yh[:, sel], Y_ref)
+    _say(f"gemm {label} M={M} N={N} K={K} bits={bits} asym={asym} {xdtype} G={G}: rel_l2={err:.2e}")
+    assert err <= REL_L2
+    return err
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 15, 16, 17, 33, 64, 65, 130])
+@pytest.mark.parametrize("xdtype", ["f16", "bf16"])
+def test_gemm_small_shapes(M, xdtype):
+    rng = np.random.default_rng(M)
+    N, K = 200, 1024 + 256
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X32 = rng.standard_normal((M, K)).astype(np.float32)
+    X = X32.astype(np.float16) if xdtype == "f16" else synth.to_bf16_bits(X32)
+    for bits in (3, 4):
+        gemm_case(W, X, xdtype, bits, True, label="small")
+    gemm_case(W, X, xdtype, 4, False, label="small")
+
+
+@pytest.mark.parametrize("G", [32, 64, 256])
+def test_gemm_group_sizes(G):
+    rng = np.random.default_rng(G + 1)
+    N, K, M = 96, 1024, 24
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    for bits in (3, 4):
+        gemm_case(W, X, "f16", bits, True, G=G, label=f"G{G}")
+
+
+def test_gemm_awq_scale():
+    lin = synth.c3_linear(6)
+    X = synth.to_f16(synth.activations_f32(8, lin.K, 77, lin.extra["channels"]))
+    gemm_case(lin.W[:300], X, "f16", 4, True, s=lin.act_scale, label="awq")
+
+
+def test_gemm_one_hot_rows():
+    rng = np.random.default_rng(5)
+    N, K = 64, 512
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    ks = [0, 1, 7, 8, 31, 32, 100, 127, 128, 300, 511]
+    X = np.zeros((len(ks), K), np.float16)
+    for m, k in enumerate(ks):
+        X[m, k] = 1.0
+    for bits in (3, 4):
+        packed, scales, zeros = ops.quantize_pack(gpu_f16(W), bits, 128, True)
+        Y = ops.gemm(gpu_f16(X), packed, scales, zeros, N, K, bits, 128).cpu().numpy()
+        q = O.quantize(W, bits, 128, True)
+        w_hat16 = O.dequantize(q).astype(np.float16)
+        for m, k in enumerate(ks):
+            assert np.array_equal(Y[m].view(np.uint16), w_hat16[:, k].view(np.uint16)), (bits, k)
+
+
+@pytest.mark.parametrize("M", [4, 16, 64])
+@pytest.mark.parametrize("xdtype", ["f16", "bf16"])
+def test_gemm_small_batch_full_size_sampled(M, xdtype):
+    lin = synth.c4_small_batch(M, xdtype)
+    rows = np.sort(np.random.default_rng(M).choice(lin.N, 192, replace=False))
+    rows = np.concatenate([rows, [lin.N - 1]])
+    gemm_case(lin.W, lin.X, xdtype, 4, True, rows=rows, label="c4")
+
+
+def test_gemm_prefill_full_size_sampled():
+    lin = synth.c5_prefill()
+    rows = np.sort(np.random.default_rng(5).choice(lin.N, 96, replace=False))
+    rows = np.concatenate([rows, [lin.N - 1]])
+    gemm_case(lin.W, lin.X, "f16", 4, True, rows=rows, label="c5")

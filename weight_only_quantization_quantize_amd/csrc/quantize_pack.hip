@@ -1,0 +1,301 @@
+// Group-wise RTN quantization of fp16 weights into layout-v1 codes plus fp16
+// scales / zero points, bit-exact with the reference definition:
+//
+//   w = fl32(W * s)                       (optional AWQ fold, one multiply)
+//   symmetric : S = f16(max|w| / (2^(b-1)-1)), u = clip(rne(w/S), -2^(b-1), 2^(b-1)-1) + 2^(b-1)
+//   asymmetric: r = max-min (1 if 0), S = f16(r / (2^b-1)),
+//               Z = clip(rne(-min/S), 0, 2^b-1), u = clip(rne(w/S) + Z, 0, 2^b-1)
+//
+// ("Quantising Large Language Models for Efficient Inference", section
+// "Post-training methods for 4-bit weights"; "CMU 11-868 L19-L20 Model
+// Quantization", section "absmax and zero-point"; "LLM Quantization: 160GB
+// Model on a Laptop", sections "Symmetric Quantization" and "Asymmetric
+// Quantization".)
+//
+// Every decision is one correctly rounded binary32 operation: IEEE division
+// (the build keeps HIP's correctly rounded fp32 divide), rintf = round half to
+// even, fp32 -> fp16 conversion round-to-nearest-even with subnormals, and no
+// FMA contraction in this file.
+//
+// Work split: one thread owns one 32-weight chunk of a row (64 B of fp16 in,
+// 16 B (4-bit) or 12 B (3-bit) of codes out).  For group sizes whose chunk
+// count divides the 64-lane wave, the chunk threads of a group reduce the
+// group statistic with lane shuffles; other group sizes use one workgroup per
+// group with an LDS reduction.  The pass is HBM-bound: 2 B read and b/8 B
+// written per weight.
+#include "woq_device.h"
+#include "woq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace woq {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <bool FOLD>
+__device__ inline void load_chunk(const uint16_t* __restrict__ W, const float* __restrict__ s, int64_t row_off,
+                                  int k0, float (&w)[32]) {
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(W + row_off + k0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4_t v = src[q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[8 * q + 2 * e] = half_bits_to_f32((uint16_t)(v[e] & 0xFFFFu));
+      w[8 * q + 2 * e + 1] = half_bits_to_f32((uint16_t)(v[e] >> 16));
+    }
+  }
+  if (FOLD) {
+    const float4_t* sp = reinterpret_cast<const float4_t*>(s + k0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4_t sv = sp[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[4 * q + e] = w[4 * q + e] * sv[e];
+    }
+  }
+}
+
+__device__ inline uint16_t f32_to_half_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Scale (and zero point) of one group from its statistic.  For the
+// symmetric form `lo` is unused and `hi` is max|w|.
+template <int BITS, bool ASYM>
+struct GroupParams {
+  float S;        // the stored fp16 scale, widened exactly
+  int Z;          // zero point (symmetric: 2^(b-1))
+  uint16_t S16;   // fp16 bits of S
+  bool zero;      // S == 0: every code is Z
+};
+
+template <int BITS, bool ASYM>
+__device__ inline GroupParams<BITS, ASYM> group_params(float lo, float hi) {
+  GroupParams<BITS, ASYM> p;
+  if (!ASYM) {
+    const float qmax = (float)((1 << (BITS - 1)) - 1);
+    p.S16 = f32_to_half_bits(hi / qmax);
+    p.S = half_bits_to_f32(p.S16);
+    p.Z = 1 << (BITS - 1);
+    p.zero = (p.S == 0.0f);
+  } else {
+    const float qu = (float)((1 << BITS) - 1);
+    float r = hi - lo;
+    if (r == 0.0f) r = 1.0f;
+    p.S16 = f32_to_half_bits(r / qu);
+    p.S = half_bits_to_f32(p.S16);
+    p.zero = (p.S == 0.0f);
+    if (p.zero) {
+      p.Z = 0;
+    } else {
+      int z = (int)__builtin_rintf(-lo / p.S);
+      p.Z = z < 0 ? 0 : (z > (1 << BITS) - 1 ? (1 << BITS) - 1 : z);
+    }
+  }
+  return p;
+}
+
+template <int BITS, bool ASYM>
+__device__ inline void codes_of_chunk(const float (&w)[32], const GroupParams<BITS, ASYM>& p, uint32_t (&u)[32]) {
+  const int top = (1 << BITS) - 1;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    int v;
+    if (p.zero) {
+      v = p.Z;
+    } else {
+      int q = (int)__builtin_rintf(w[i] / p.S);
+      if (!ASYM) {
+        const int h = 1 << (BITS - 1);
+        q = q < -h ? -h : (q > h - 1 ? h - 1 : q);
+        v = q + h;
+      } else {
+        v = q + p.Z;
+        v = v < 0 ? 0 : (v > top ? top : v);
+      }
+    }
+    u[i] = (uint32_t)v;
+  }
+}
+
+template <int BITS>
+__device__ inline void store_chunk(uint8_t* __restrict__ packed, int64_t n, int K, int kc, const uint32_t (&u)[32]) {
+  if (BITS == 4) {
+    u32x4_t out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) word |= u[8 * j + 2 * t + h] << (16 * h + 4 * t);
+      out[j] = word;
+    }
+    *reinterpret_cast<u32x4_t*>(packed + n * (int64_t)(K / 2) + (int64_t)kc * 16) = out;
+  } else {
+    uint32_t w0 = 0, w1 = 0, w2 = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int t = i >> 1, h = i & 1;
+      const uint32_t lo = (u[i] & 3u) << (16 * h + 2 * (t & 7));
+      if (t < 8) w0 |= lo; else w1 |= lo;
+      w2 |= ((u[i] >> 2) & 1u) << (16 * h + t);
+    }
+    uint32_t* dst = reinterpret_cast<uint32_t*>(packed + n * (int64_t)(3 * K / 8) + (int64_t)kc * 12);
+    dst[0] = w0;
+    dst[1] = w1;
+    dst[2] = w2;
+  }
+}
+
+// Group of `team` consecutive chunk threads (team = G/32 divides 64).
+template <int BITS, bool ASYM, bool FOLD>
+__global__ __launch_bounds__(kThreads) void quantize_pack_team_kernel(
+    const uint16_t* __restrict__ W, const float* __restrict__ s, int64_t total_chunks, int K, int G, int team,
+    uint8_t* __restrict__ packed, uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool valid = c < total_chunks;
+  const int cpr = K >> 5;
+  const int64_t n = valid ? c / cpr : 0;
+  const int kc = valid ? (int)(c - n * cpr) : 0;
+  float w[32];
+  if (valid) {
+    load_chunk<FOLD>(W, s, n * (int64_t)K, kc * 32, w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i] = 0.0f;
+  }
+  float lo = 0.0f, hi = 0.0f;
+  if (!ASYM) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) hi = fmaxf(hi, fabsf(w[i]));
+    hi = team_max(hi, team);
+  } else {
+    lo = w[0];
+    hi = w[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) {
+      lo = fminf(lo, w[i]);
+      hi = fmaxf(hi, w[i]);
+    }
+    lo = team_min(lo, team);
+    hi = team_max(hi, team);
+  }
+  if (!valid) return;
+  const GroupParams<BITS, ASYM> p = group_params<BITS, ASYM>(lo, hi);
+  uint32_t u[32];
+  codes_of_chunk<BITS, ASYM>(w, p, u);
+  store_chunk<BITS>(packed, n, K, kc, u);
+  if ((kc & (team - 1)) == 0) {
+    const int64_t gi = n * (int64_t)(K / G) + (kc * 32) / G;
+    scales[gi] = p.S16;
+    if (ASYM) zeros[gi] = f32_to_half_bits((float)p.Z);
+  }
+}
+
+// One workgroup per group (any G that is a multiple of 32).
+template <int BITS, bool ASYM, bool FOLD>
+__global__ __launch_bounds__(kThreads) void quantize_pack_block_kernel(
+    const uint16_t* __restrict__ W, const float* __restrict__ s, int K, int G, uint8_t* __restrict__ packed,
+    uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
+  __shared__ float red_lo[kThreads / 64], red_hi[kThreads / 64];
+  const int groups_per_row = K / G;
+  const int64_t gid = blockIdx.x;
+  const int64_t n = gid / groups_per_row;
+  const int g = (int)(gid - n * groups_per_row);
+  const int chunks = G >> 5;
+  const int c0 = g * chunks;  // first chunk of the group within the row
+  float lo = 0.0f, hi = 0.0f;
+  bool first = true;
+  for (int c = threadIdx.x; c < chunks; c += kThreads) {
+    float w[32];
+    load_chunk<FOLD>(W, s, n * (int64_t)K, (c0 + c) * 32, w);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (!ASYM) {
+        hi = fmaxf(hi, fabsf(w[i]));
+      } else if (first && i == 0) {
+        lo = w[0];
+        hi = w[0];
+      } else {
+        lo = fminf(lo, w[i]);
+        hi = fmaxf(hi, w[i]);
+      }
+    }
+    first = false;
+  }
+  // Threads that own no chunk must not disturb the asymmetric min / max.
+  if (ASYM && first) {
+    lo = __builtin_huge_valf();
+    hi = -__builtin_huge_valf();
+  }
+  lo = team_min(lo, 64);
+  hi = team_max(hi, 64);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red_lo[wave] = lo;
+    red_hi[wave] = hi;
+  }
+  __syncthreads();
+  lo = red_lo[0];
+  hi = red_hi[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) {
+    lo = fminf(lo, red_lo[i]);
+    hi = fmaxf(hi, red_hi[i]);
+  }
+  const GroupParams<BITS, ASYM> p = group_params<BITS, ASYM>(lo, hi);
+  for (int c = threadIdx.x; c < chunks; c += kThreads) {
+    float w[32];
+    load_chunk<FOLD>(W, s, n * (int64_t)K, (c0 + c) * 32, w);
+    uint32_t u[32];
+    codes_of_chunk<BITS, ASYM>(w, p, u);
+    store_chunk<BITS>(packed, n, K, c0 + c, u);
+  }
+  if (threadIdx.x == 0) {
+    scales[gid] = p.S16;
+    if (ASYM) zeros[gid] = f32_to_half_bits((float)p.Z);
+  }
+}
+
+template <int BITS, bool ASYM, bool FOLD>
+hipError_t launch_typed(const void* W, const float* s, int64_t N, int64_t K, int G, void* packed, void* scales,
+                        void* zeros, hipStream_t stream) {
+  const int team = G / 32;
+  if (team <= 64 && (64 % team) == 0) {
+    const int64_t total = N * (K / 32);
+    const int64_t blocks = (total + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL((quantize_pack_team_kernel<BITS, ASYM, FOLD>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, static_cast<const uint16_t*>(W), s, total, (int)K, G, team,
+                       static_cast<uint8_t*>(packed), static_cast<uint16_t*>(scales),
+                       static_cast<uint16_t*>(zeros));
+  } else {
+    const int64_t groups = N * (K / G);
+    hipLaunchKernelGGL((quantize_pack_block_kernel<BITS, ASYM, FOLD>), dim3((unsigned)groups), dim3(kThreads), 0,
+                       stream, static_cast<const uint16_t*>(W), s, (int)K, G, static_cast<uint8_t*>(packed),
+                       static_cast<uint16_t*>(scales), static_cast<uint16_t*>(zeros));
+  }
+  return hipGetLastError();
+}
+
+template <int BITS, bool ASYM>
+hipError_t launch_fold(const void* W, const float* s, int64_t N, int64_t K, int G, void* packed, void* scales,
+                       void* zeros, hipStream_t stream) {
+  return s ? launch_typed<BITS, ASYM, true>(W, s, N, K, G, packed, scales, zeros, stream)
+           : launch_typed<BITS, ASYM, false>(W, s, N, K, G, packed, scales, zeros, stream);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_pack(const void* W, const float* act_scale, int64_t N, int64_t K, int bits,
+                                int group_size, bool asymmetric, void* packed, void* scales, void* zeros,
+                                hipStream_t stream) {
+  if (bits == 4) {
+    return asymmetric ? launch_fold<4, true>(W, act_scale, N, K, group_size, packed, scales, zeros, stream)
+                      : launch_fold<4, false>(W, act_scale, N, K, group_size, packed, scales, zeros, stream);
+  }
+  return asymmetric ? launch_fold<3, true>(W, act_scale, N, K, group_size, packed, scales, zeros, stream)
+                    : launch_fold<3, false>(W, act_scale, N, K, group_size, packed, scales, zeros, stream);
+}
+
+}  // namespace woq

@@ -1,0 +1,221 @@
+// C ABI of libwoq: argument validation, kernel dispatch and error reporting.
+// Declarations and the contract of every entry point are in include/woq.h.
+#include "../../include/woq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+#include <string>
+
+#include "woq_internal.h"
+
+namespace woq {
+int gemv_max_k();
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+
+woq_status fail(woq_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+woq_status fail(woq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+woq_status ok() {
+  g_last_error.clear();
+  return WOQ_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks shared by every entry point that takes a packed matrix.
+woq_status check_qparams(int64_t N, int64_t K, int32_t bits, int32_t group_size) {
+  if (bits != 3 && bits != 4) return fail(WOQ_ERR_INVALID_ARGUMENT, "bits must be 3 or 4 (got %d)", bits);
+  if (N < 1) return fail(WOQ_ERR_INVALID_ARGUMENT, "N must be >= 1 (got %lld)", (long long)N);
+  if (K < 32 || K % 32 != 0)
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "K must be a positive multiple of 32 (got %lld)", (long long)K);
+  if (group_size < 32 || group_size % 32 != 0)
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "group_size must be a positive multiple of 32 (got %d)", group_size);
+  if (K % group_size != 0)
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "K (%lld) must be a multiple of group_size (%d)", (long long)K,
+                group_size);
+  if (N > INT32_MAX || K > INT32_MAX / 2)
+    return fail(WOQ_ERR_UNSUPPORTED, "N or K too large for this build (N=%lld, K=%lld)", (long long)N,
+                (long long)K);
+  return WOQ_OK;
+}
+
+woq_status check_packed_inputs(const void* packed, const void* scales, const void* zeros, int32_t asymmetric) {
+  if (!packed || !scales) return fail(WOQ_ERR_INVALID_ARGUMENT, "packed and scales must not be NULL");
+  if (!aligned(packed, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "packed must be 16-byte aligned");
+  if (!aligned(scales, 2)) return fail(WOQ_ERR_INVALID_ARGUMENT, "scales must be 2-byte aligned");
+  if (asymmetric && !zeros) return fail(WOQ_ERR_INVALID_ARGUMENT, "zeros must not be NULL when asymmetric");
+  if (!asymmetric && zeros) return fail(WOQ_ERR_INVALID_ARGUMENT, "zeros must be NULL when symmetric");
+  if (zeros && !aligned(zeros, 2)) return fail(WOQ_ERR_INVALID_ARGUMENT, "zeros must be 2-byte aligned");
+  return WOQ_OK;
+}
+
+woq_status check_act_scale(const float* act_scale) {
+  if (act_scale && !aligned(act_scale, 16))
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "act_scale must be 16-byte aligned");
+  return WOQ_OK;
+}
+
+woq_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(WOQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define WOQ_TRY(expr)                   \
+  do {                                  \
+    const woq_status st_ = (expr);      \
+    if (st_ != WOQ_OK) return st_;      \
+  } while (0)
+
+#define WOQ_GUARD_BEGIN try {
+#define WOQ_GUARD_END                                                        \
+  }                                                                          \
+  catch (const std::exception& e) {                                          \
+    return fail(WOQ_ERR_INTERNAL, "internal error: %s", e.what());           \
+  }                                                                          \
+  catch (...) {                                                              \
+    return fail(WOQ_ERR_INTERNAL, "internal error: unknown exception");      \
+  }
+
+}  // namespace
+
+extern "C" {
+
+int32_t woq_layout_version(void) { return WOQ_LAYOUT_V1; }
+
+size_t woq_packed_bytes(int64_t N, int64_t K, int32_t bits) {
+  if ((bits != 3 && bits != 4) || N < 1 || K < 32 || K % 32 != 0) return 0;
+  return (size_t)N * (size_t)K * (size_t)bits / 8;
+}
+
+size_t woq_scales_bytes(int64_t N, int64_t K, int32_t group_size) {
+  if (N < 1 || K < 1 || group_size < 1 || K % group_size != 0) return 0;
+  return (size_t)N * (size_t)(K / group_size) * 2;
+}
+
+size_t woq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size) {
+  (void)M;
+  (void)N;
+  (void)K;
+  (void)bits;
+  (void)group_size;
+  return 0;
+}
+
+woq_status woq_quantize_pack(const void* W, const float* act_scale, int64_t N, int64_t K, int32_t bits,
+                             int32_t group_size, int32_t asymmetric, void* packed, void* scales, void* zeros,
+                             void* stream) {
+  WOQ_GUARD_BEGIN
+  WOQ_TRY(check_qparams(N, K, bits, group_size));
+  if (!W) return fail(WOQ_ERR_INVALID_ARGUMENT, "W must not be NULL");
+  if (!aligned(W, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "W must be 16-byte aligned");
+  WOQ_TRY(check_packed_inputs(packed, scales, zeros, asymmetric));
+  WOQ_TRY(check_act_scale(act_scale));
+  return from_hip(woq::launch_quantize_pack(W, act_scale, N, K, bits, group_size, asymmetric != 0, packed, scales,
+                                            zeros, static_cast<hipStream_t>(stream)),
+                  "quantize_pack launch");
+  WOQ_GUARD_END
+}
+
+woq_status woq_w4a16_gemv(const void* x, int32_t xdtype, const float* act_scale, const void* packed,
+                          const void* scales, const void* zeros, int64_t N, int64_t K, int32_t bits,
+                          int32_t group_size, int32_t asymmetric, void* y, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  WOQ_GUARD_BEGIN
+  (void)workspace;
+  (void)workspace_bytes;
+  WOQ_TRY(check_qparams(N, K, bits, group_size));
+  if (xdtype != WOQ_F16 && xdtype != WOQ_BF16)
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "xdtype must be WOQ_F16 or WOQ_BF16 (got %d)", xdtype);
+  if (!x || !y) return fail(WOQ_ERR_INVALID_ARGUMENT, "x and y must not be NULL");
+  if (!aligned(x, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "x must be 16-byte aligned");
+  if (!aligned(y, 2)) return fail(WOQ_ERR_INVALID_ARGUMENT, "y must be 2-byte aligned");
+  WOQ_TRY(check_packed_inputs(packed, scales, zeros, asymmetric));
+  WOQ_TRY(check_act_scale(act_scale));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (K <= woq::gemv_max_k())
+    return from_hip(woq::launch_gemv(x, xdtype, act_scale, packed, scales, zeros, N, K, bits, group_size,
+                                     asymmetric != 0, y, st),
+                    "gemv launch");
+  return from_hip(woq::launch_gemm(x, xdtype, act_scale, packed, scales, zeros, 1, N, K, bits, group_size,
+                                   asymmetric != 0, y, st),
+                  "gemv (long K) launch");
+  WOQ_GUARD_END
+}
+
+woq_status woq_w4a16_gemm(const void* X, int32_t xdtype, const float* act_scale, const void* packed,
+                          const void* scales, const void* zeros, int64_t M, int64_t N, int64_t K, int32_t bits,
+                          int32_t group_size, int32_t asymmetric, void* Y, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  WOQ_GUARD_BEGIN
+  (void)workspace;
+  (void)workspace_bytes;
+  WOQ_TRY(check_qparams(N, K, bits, group_size));
+  if (M < 1) return fail(WOQ_ERR_INVALID_ARGUMENT, "M must be >= 1 (got %lld)", (long long)M);
+  if (M > INT32_MAX / 2) return fail(WOQ_ERR_UNSUPPORTED, "M too large for this build (%lld)", (long long)M);
+  if (xdtype != WOQ_F16 && xdtype != WOQ_BF16)
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "xdtype must be WOQ_F16 or WOQ_BF16 (got %d)", xdtype);
+  if (!X || !Y) return fail(WOQ_ERR_INVALID_ARGUMENT, "X and Y must not be NULL");
+  if (!aligned(X, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "X must be 16-byte aligned");
+  if (!aligned(Y, 2)) return fail(WOQ_ERR_INVALID_ARGUMENT, "Y must be 2-byte aligned");
+  WOQ_TRY(check_packed_inputs(packed, scales, zeros, asymmetric));
+  WOQ_TRY(check_act_scale(act_scale));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (M == 1 && K <= woq::gemv_max_k())
+    return from_hip(woq::launch_gemv(X, xdtype, act_scale, packed, scales, zeros, N, K, bits, group_size,
+                                     asymmetric != 0, Y, st),
+                    "gemm (M=1) launch");
+  return from_hip(woq::launch_gemm(X, xdtype, act_scale, packed, scales, zeros, M, N, K, bits, group_size,
+                                   asymmetric != 0, Y, st),
+                  "gemm launch");
+  WOQ_GUARD_END
+}
+
+woq_status woq_dequantize(const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K,
+                          int32_t bits, int32_t group_size, int32_t asymmetric, float* out, void* stream) {
+  WOQ_GUARD_BEGIN
+  WOQ_TRY(check_qparams(N, K, bits, group_size));
+  WOQ_TRY(check_packed_inputs(packed, scales, zeros, asymmetric));
+  if (!out) return fail(WOQ_ERR_INVALID_ARGUMENT, "out must not be NULL");
+  if (!aligned(out, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
+  return from_hip(woq::launch_dequantize(packed, scales, zeros, N, K, bits, group_size, asymmetric != 0, out,
+                                         static_cast<hipStream_t>(stream)),
+                  "dequantize launch");
+  WOQ_GUARD_END
+}
+
+const char* woq_status_string(woq_status status) {
+  switch (status) {
+    case WOQ_OK:
+      return "WOQ_OK";
+    case WOQ_ERR_INVALID_ARGUMENT:
+      return "WOQ_ERR_INVALID_ARGUMENT";
+    case WOQ_ERR_UNSUPPORTED:
+      return "WOQ_ERR_UNSUPPORTED";
+    case WOQ_ERR_HIP:
+      return "WOQ_ERR_HIP";
+    case WOQ_ERR_INTERNAL:
+      return "WOQ_ERR_INTERNAL";
+  }
+  return "WOQ_ERR_UNKNOWN";
+}
+
+const char* woq_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

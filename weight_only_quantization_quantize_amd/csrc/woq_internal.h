@@ -1,0 +1,32 @@
+// Internal interface between the C ABI layer (woq_api.cpp) and the kernel
+// translation units.  Every launcher assumes its arguments were validated by
+// the ABI layer and returns the HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace woq {
+
+// Quantize + pack (one thread per 32-weight chunk; groups reduced across the
+// chunk threads of the group).
+hipError_t launch_quantize_pack(const void* W, const float* act_scale, int64_t N, int64_t K, int bits,
+                                int group_size, bool asymmetric, void* packed, void* scales, void* zeros,
+                                hipStream_t stream);
+
+// M = 1 GEMV.  xdtype: 0 = fp16, 1 = bf16.
+hipError_t launch_gemv(const void* x, int xdtype, const float* act_scale, const void* packed,
+                       const void* scales, const void* zeros, int64_t N, int64_t K, int bits,
+                       int group_size, bool asymmetric, void* y, hipStream_t stream);
+
+// M >= 1 GEMM.
+hipError_t launch_gemm(const void* X, int xdtype, const float* act_scale, const void* packed,
+                       const void* scales, const void* zeros, int64_t M, int64_t N, int64_t K, int bits,
+                       int group_size, bool asymmetric, void* Y, hipStream_t stream);
+
+// Dequantize to fp32 (test aid).
+hipError_t launch_dequantize(const void* packed, const void* scales, const void* zeros, int64_t N,
+                             int64_t K, int bits, int group_size, bool asymmetric, float* out,
+                             hipStream_t stream);
+
+}  // namespace woq

@@ -1,0 +1,136 @@
+"""PyTorch-facing wrappers over the C ABI.
+
+PyTorch provides device memory and the current HIP stream; each function
+checks tensor shapes / dtypes / devices, then passes raw pointers to the
+library.  Nothing is computed here.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DTYPE = {torch.float16: _lib.WOQ_F16, torch.bfloat16: _lib.WOQ_BF16}
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require_gpu(*ts: Optional[torch.Tensor]) -> None:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libwoq works on GPU tensors only")
+        if not t.is_contiguous():
+            raise ValueError("libwoq needs contiguous tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+
+
+def packed_bytes(N: int, K: int, bits: int) -> int:
+    return int(_lib.call("woq_packed_bytes", N, K, bits))
+
+
+def quantize_pack(
+    W: torch.Tensor,
+    bits: int = 4,
+    group_size: int = 128,
+    asymmetric: bool = True,
+    act_scale: Optional[torch.Tensor] = None,
+    out: Optional[Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]] = None,
+):
+    """Quantize fp16 W [N, K] -> (packed uint8 [N, K*bits/8], scales fp16 [N, K/G], zeros fp16 | None)."""
+    if W.dtype != torch.float16 or W.dim() != 2:
+        raise ValueError("W must be a 2-D float16 tensor")
+    N, K = W.shape
+    if act_scale is not None and (act_scale.dtype != torch.float32 or act_scale.shape != (K,)):
+        raise ValueError("act_scale must be float32 [K]")
+    if out is None:
+        packed = torch.empty((N, K * bits // 8), dtype=torch.uint8, device=W.device)
+        scales = torch.empty((N, K // group_size), dtype=torch.float16, device=W.device)
+        zeros = torch.empty_like(scales) if asymmetric else None
+    else:
+        packed, scales, zeros = out
+    _require_gpu(W, act_scale, packed, scales, zeros)
+    st = _lib.call("woq_quantize_pack", W.data_ptr(), _ptr(act_scale), N, K, bits, group_size, int(asymmetric),
+                   packed.data_ptr(), scales.data_ptr(), _ptr(zeros), _stream(W))
+    _lib.check(st, "woq_quantize_pack")
+    return packed, scales, zeros
+
+
+def gemv(
+    x: torch.Tensor,
+    packed: torch.Tensor,
+    scales: torch.Tensor,
+    zeros: Optional[torch.Tensor],
+    N: int,
+    K: int,
+    bits: int = 4,
+    group_size: int = 128,
+    act_scale: Optional[torch.Tensor] = None,
+    out: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """y [N] = (x / s) @ w_hat^T for x [K] (fp16 or bf16)."""
+    if x.dtype not in _DTYPE or x.numel() != K:
+        raise ValueError("x must be fp16/bf16 with K elements")
+    y = out if out is not None else torch.empty((N,), dtype=x.dtype, device=x.device)
+    _require_gpu(x, act_scale, packed, scales, zeros, y)
+    st = _lib.call("woq_w4a16_gemv", x.data_ptr(), _DTYPE[x.dtype], _ptr(act_scale), packed.data_ptr(),
+                   scales.data_ptr(), _ptr(zeros), N, K, bits, group_size, int(zeros is not None), y.data_ptr(),
+                   None, 0, _stream(x))
+    _lib.check(st, "woq_w4a16_gemv")
+    return y
+
+
+def gemm(
+    X: torch.Tensor,
+    packed: torch.Tensor,
+    scales: torch.Tensor,
+    zeros: Optional[torch.Tensor],
+    N: int,
+    K: int,
+    bits: int = 4,
+    group_size: int = 128,
+    act_scale: Optional[torch.Tensor] = None,
+    out: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """Y [M, N] = (X / s) @ w_hat^T for X [M, K] (fp16 or bf16)."""
+    if X.dtype not in _DTYPE or X.dim() != 2 or X.shape[1] != K:
+        raise ValueError("X must be fp16/bf16 [M, K]")
+    M = X.shape[0]
+    Y = out if out is not None else torch.empty((M, N), dtype=X.dtype, device=X.device)
+    _require_gpu(X, act_scale, packed, scales, zeros, Y)
+    st = _lib.call("woq_w4a16_gemm", X.data_ptr(), _DTYPE[X.dtype], _ptr(act_scale), packed.data_ptr(),
+                   scales.data_ptr(), _ptr(zeros), M, N, K, bits, group_size, int(zeros is not None), Y.data_ptr(),
+                   None, 0, _stream(X))
+    _lib.check(st, "woq_w4a16_gemm")
+    return Y
+
+
+def dequantize(
+    packed: torch.Tensor,
+    scales: torch.Tensor,
+    zeros: Optional[torch.Tensor],
+    N: int,
+    K: int,
+    bits: int = 4,
+    group_size: int = 128,
+) -> torch.Tensor:
+    """w_hat = (u - Z) * S as float32 [N, K]."""
+    out = torch.empty((N, K), dtype=torch.float32, device=packed.device)
+    _require_gpu(packed, scales, zeros, out)
+    st = _lib.call("woq_dequantize", packed.data_ptr(), scales.data_ptr(), _ptr(zeros), N, K, bits, group_size,
+                   int(zeros is not None), out.data_ptr(), _stream(packed))
+    _lib.check(st, "woq_dequantize")
+    return out

@@ -123,13 +123,9 @@ __global__ __launch_bounds__(kThreads) void gemm_direct_kernel(
     const int kbeg = kb + lg * (KB / 4);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      // columns past N load row N-1 (always valid); their results are never stored
       const int n = nw + 16 * nt + lr;
-      if (n < N) {
-        load_b<BITS, KB>(packed, n, K, kbeg, bc[nt]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < (int)(sizeof(bc[nt].w) / 4); ++j) bc[nt].w[j] = 0u;
-      }
+      load_b<BITS, KB>(packed, n < N ? n : N - 1, K, kbeg, bc[nt]);
     }
 
     __syncthreads();  // previous block's LDS readers are done

@@ -3,209 +3,318 @@
 // Decode is memory-bound: a [1, K] x [K, N] GEMV does about one flop per byte
 // of weights ("MIT 6.5940 Lab 4 + Lab 5", Lab 4 "Starting point and setup";
 // "CMU 11-868 L19-L20", section "Back to the question: where does the speed
-// come from?"), so the kernel is built to stream the packed codes from HBM
-// exactly once and dequantize them in registers ("Quantising Large Language
-// Models ...", section "Weight-only vs weight-and-activation quantisation").
+// come from?"), so the kernel streams the packed codes from HBM exactly once
+// and dequantizes them in registers ("Quantising Large Language Models ...",
+// section "Weight-only vs weight-and-activation quantisation").
 //
-// Mapping (one 64-lane wave per output row, or per 64/team rows when a row
-// has fewer than 64 chunks of 32 weights):
-//  * a team of `team` lanes covers one row; lane p of the team owns chunks
-//    c = i*team + p (i < CPL) of every row, i.e. a fixed slice of K;
-//  * that slice of x (divided by the AWQ scale when given, rounded once to
-//    the activation type) lives in registers for the whole kernel, together
-//    with the fp32 sum of each chunk's 32 activations;
-//  * per row the team issues CPL lane-contiguous loads (16 B per lane for
-//    4-bit, 12 B for 3-bit: a team reads a contiguous stretch of the row) plus
-//    the fp16 scale / zero of each chunk's group;
-//  * a code pair is turned into the 16-bit float pair (MAGIC + u) by one
-//    shift / mask / OR, multiplied into fp32 with v_dot2 against the matching
-//    activation pair, and the chunk total is corrected and scaled in fp32:
-//      S * (sum x (MAGIC + u) - (MAGIC + Z) * sum x) = S * sum x (u - Z);
-//  * the team reduces its partial sums with lane shuffles and one lane writes
-//    y[n] rounded to the activation type.
+// Work split.  A row of K weights is cut into segments of up to 64 chunks of
+// 32 weights (one 16-byte / 12-byte load per lane per segment).  A workgroup
+// holds RPB rows x SPR segments, one wave per (row, segment); lane p of the
+// wave for segment g always owns chunk 64 g + p, so its 32 activations are
+// read once (from x / s staged in LDS) and stay in 16 registers.
+//
+// Order of the stream.  Workgroup b handles the row groups b, b + B, b + 2B,
+// ... (B = number of workgroups), so at every step the whole GPU reads one
+// contiguous window of B * RPB rows; each wave keeps kPrefetch steps of code
+// loads in flight ahead of the step it computes.
+//
+// Decode.  fp16 activations: a masked 4-bit code pair (w & 0x000F000F, or
+// w & 0x00F000F0 for the pair one nibble up) is read by v_dot2 as two fp16
+// subnormals of value u * 2^-24 (resp. 16u * 2^-24), which v_dot2 multiplies
+// exactly; one AND per pair and
+//   sum x (u - Z) = 2^24 (a + b / 16) - Z * sum x.
+// 3-bit pairs are reassembled in the low bits the same way.  bf16 activations
+// OR the pair into the 16-bit float MAGIC + u (0x4300 = 128) and remove
+// (MAGIC + Z) * sum x instead.
+//
+// Reduction.  Each lane keeps one fp32 partial per step in LDS; after the
+// stream each wave sums the partials of a few outputs with one DPP reduction,
+// so no cross-lane work interrupts the stream.
 #include "woq_device.h"
 #include "woq_internal.h"
 
 namespace woq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kMaxSegments = 8;      // K <= 8 * 64 * 32 = 16384 on this path
+constexpr int kTargetWaves = 8;      // waves per workgroup
+constexpr int kTargetBlocks = 1024;  // workgroups sweeping the matrix together
+constexpr int kPrefetch = 2;         // steps of code loads in flight ahead of compute
 
-template <int BITS>
-struct ChunkCodes;
-template <>
-struct ChunkCodes<4> {
-  uint32_t w[4];
-};
-template <>
-struct ChunkCodes<3> {
-  uint32_t w[3];
+struct __attribute__((packed, aligned(4))) U32x3 {
+  uint32_t a, b, c;
 };
 
 template <int BITS>
-__device__ inline void load_codes(const uint8_t* __restrict__ packed, int64_t n, int K, int c, ChunkCodes<BITS>& cc) {
-  if (BITS == 4) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(packed + n * (int64_t)(K / 2) + (int64_t)c * 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) cc.w[j] = v[j];
+struct Codes;
+template <>
+struct Codes<4> {
+  u32x4_t w;
+};
+template <>
+struct Codes<3> {
+  uint32_t w0, w1, w2;
+};
+
+template <int BITS>
+__device__ inline void load_codes(const uint8_t* __restrict__ p, Codes<BITS>& c) {
+  if constexpr (BITS == 4) {
+    c.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   } else {
-    const uint32_t* p = reinterpret_cast<const uint32_t*>(packed + n * (int64_t)(3 * K / 8) + (int64_t)c * 12);
-#pragma unroll
-    for (int j = 0; j < 3; ++j) cc.w[j] = p[j];
+    const U32x3 v = *reinterpret_cast<const U32x3*>(p);
+    c.w0 = v.a;
+    c.w1 = v.b;
+    c.w2 = v.c;
   }
 }
 
-// sum over the chunk of x (MAGIC + u), accumulated in fp32 by v_dot2.
+// A constant the compiler cannot fold: keeps MAGIC in a VGPR so that
+// (w & mask) | MAGIC becomes one v_and_or_b32 with the mask in an SGPR.
+__device__ inline uint32_t vgpr_const(uint32_t v) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
+// Activation sums of one chunk: part[0] over the pairs t = 0, 2 of every
+// 8-weight word, part[1] over t = 1, 3.
+struct XSums {
+  float part[2];
+};
+
+// sum over the chunk of x (u - Z), before the scale S.
 template <int BITS, class XT>
-__device__ inline float chunk_dot(const ChunkCodes<BITS>& cc, const uint32_t (&xr)[16]) {
-  float a = 0.0f;
-  if (BITS == 4) {
+__device__ inline float chunk_dot(const Codes<BITS>& c, const uint32_t (&xr)[16], const XSums& xs, float Z,
+                                  uint32_t magic) {
+  constexpr bool kF16 = XT::kMagic2 == F16::kMagic2;
+  if constexpr (BITS == 4 && kF16) {
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = c.w[j], w8 = w >> 8;
+      a = XT::dot2(w & 0x000F000Fu, xr[4 * j + 0], a);   // u * 2^-24, pair t = 0
+      b = XT::dot2(w & 0x00F000F0u, xr[4 * j + 1], b);   // 16u * 2^-24, pair t = 1
+      a = XT::dot2(w8 & 0x000F000Fu, xr[4 * j + 2], a);  // pair t = 2
+      b = XT::dot2(w8 & 0x00F000F0u, xr[4 * j + 3], b);  // pair t = 3
+    }
+    return 16777216.0f * (a + 0.0625f * b) - Z * (xs.part[0] + xs.part[1]);
+  } else if constexpr (BITS == 4) {
+    float a = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) a = XT::dot2(pair4(cc.w[j], t, XT::kMagic2), xr[4 * j + t], a);
+      for (int t = 0; t < 4; ++t) a = XT::dot2(((c.w[j] >> (4 * t)) & 0x000F000Fu) | magic, xr[4 * j + t], a);
+    return a - (XT::kMagic + Z) * (xs.part[0] + xs.part[1]);
+  } else if constexpr (kF16) {
+    float a = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) a = XT::dot2(pair3(c.w0, c.w1, c.w2, t, 0u), xr[t], a);
+    return 16777216.0f * a - Z * (xs.part[0] + xs.part[1]);
   } else {
+    float a = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) a = XT::dot2(pair3(cc.w[0], cc.w[1], cc.w[2], t, XT::kMagic2), xr[t], a);
+    for (int t = 0; t < 16; ++t) a = XT::dot2(pair3(c.w0, c.w1, c.w2, t, 0u) | magic, xr[t], a);
+    return a - (XT::kMagic + Z) * (xs.part[0] + xs.part[1]);
   }
-  return a;
 }
 
-template <int BITS, bool ASYM, class XT, int CPL, bool SCALE, int ROWS>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const uint16_t* __restrict__ x, const float* __restrict__ s,
-                                                        const uint8_t* __restrict__ packed,
-                                                        const uint16_t* __restrict__ scales,
-                                                        const uint16_t* __restrict__ zeros, int N, int K, int G,
-                                                        int team_log2, uint16_t* __restrict__ y) {
+// v + (v taken from the lane the DPP control selects; 0 where there is none).
+template <int CTRL, int ROW_MASK>
+__device__ inline float add_dpp(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                                                   0xf, true));
+}
+
+// Full 64-lane sum; the total lands in lane 63.
+__device__ inline float wave_sum_lane63(float v) {
+  v = add_dpp<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+  v = add_dpp<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+  v = add_dpp<0x114, 0xf>(v);  // row_shr:4
+  v = add_dpp<0x118, 0xf>(v);  // row_shr:8
+  v = add_dpp<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = add_dpp<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+template <int BITS>
+struct StepLoads {
+  Codes<BITS> c;
+  uint16_t s16, z16;
+};
+
+// Dynamic LDS layout: x' (padded to PASSES * threads 16-byte units) |
+// partials [STEPS][waves][64] floats.
+//
+// SPR_T > 0 fixes the shape at compile time: K = 2048 * SPR_T (every segment
+// full), group size 128, RPB = max(1, 8 / SPR_T) rows per workgroup.  SPR_T == 0
+// is the general path (any K <= 16384 that is a multiple of 32, any group
+// size that is a multiple of 32), with the shape passed at run time.
+template <int BITS, bool ASYM, class XT, bool SCALE, int STEPS, int SPR_T, int PASSES>
+__global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__ x, const float* __restrict__ s,
+                                                    const uint8_t* __restrict__ packed,
+                                                    const uint16_t* __restrict__ scales,
+                                                    const uint16_t* __restrict__ zeros, int N, int K_rt, int G_rt,
+                                                    int spr_rt, int rpb_rt, uint16_t* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  constexpr bool kFixed = SPR_T > 0;
+  const int K = kFixed ? 2048 * SPR_T : K_rt;
+  const int G = kFixed ? 128 : G_rt;
+  const int spr = kFixed ? SPR_T : spr_rt;
+  const int rpb = kFixed ? (SPR_T >= 8 ? 1 : 8 / SPR_T) : rpb_rt;
+  const int nthreads = kFixed ? rpb * spr * 64 : (int)blockDim.x;
+  const int cpr = K >> 5;  // chunks per row
+  uint32_t* xsh = lds;
+  float* part = reinterpret_cast<float*>(lds + PASSES * nthreads * 4);
+  const int waves = nthreads >> 6;
   const int lane = threadIdx.x & 63;
-  const int team = 1 << team_log2;
-  const int p = lane & (team - 1);
-  const int r = lane >> team_log2;
-  const int rps = 64 >> team_log2;  // rows per wave step
-  const int cpr = K >> 5;           // chunks per row
-  const int gpr = K / G;            // groups per row
-  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int waves = gridDim.x * kWaves;
+  // wave-uniform values live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int seg = wave % spr, rr = wave / spr;  // K segment and row slot of this wave
+  const int c_raw = 64 * seg + lane;            // this lane's chunk
+  const bool live = kFixed || c_raw < cpr;
+  const int c = live ? c_raw : cpr - 1;         // clamped: every load stays inside the row
+  const int cg = (32 * c) / G;                  // its group within the row
+  const int gpr = K / G;
+  const int64_t row_bytes = (int64_t)K * BITS / 8;
+  const uint8_t* lane_codes = packed + (int64_t)c * (BITS == 4 ? 16 : 12);
+  const int row_first = (int)blockIdx.x * rpb + rr;
+  const int row_step = (int)gridDim.x * rpb;
 
-  // Activation slice of this lane, resident for the whole kernel.
-  uint32_t xr[CPL][16];
-  float xsum[CPL];
+  StepLoads<BITS> L[STEPS];
+  auto issue = [&](int st) {
+    int n = row_first + st * row_step;
+    n = n < N ? n : N - 1;
+    load_codes<BITS>(lane_codes + (int64_t)n * row_bytes, L[st].c);
+    const int64_t gi = (int64_t)n * gpr + cg;
+    L[st].s16 = scales[gi];
+    if (ASYM) L[st].z16 = zeros[gi];
+  };
+
+  // x loads first, then the first code loads: waiting for x (the memory
+  // counter drains in issue order) does not wait for the codes.
+  const int units = K >> 3;  // 16-byte units of x
+  u32x4_t xv[PASSES];
+  float4_t sv[PASSES][2];
+#pragma unroll
+  for (int it = 0; it < PASSES; ++it) {
+    int i = threadIdx.x + it * nthreads;
+    i = i < units ? i : units - 1;
+    xv[it] = reinterpret_cast<const u32x4_t*>(x)[i];
+    if (SCALE) {
+      sv[it][0] = reinterpret_cast<const float4_t*>(s)[2 * i];
+      sv[it][1] = reinterpret_cast<const float4_t*>(s)[2 * i + 1];
+    }
+  }
+#pragma unroll
+  for (int st = 0; st < kPrefetch && st < STEPS; ++st) issue(st);
+
+  // Stage x' = x / s, rounded once to the activation type, in LDS.
+#pragma unroll
+  for (int it = 0; it < PASSES; ++it) {
+    const int i = threadIdx.x + it * nthreads;
+    u32x4_t v = xv[it];
+    if (SCALE) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a0 = XT::to_f32((uint16_t)(v[e] & 0xFFFFu)) / sv[it][e / 2][(2 * e) % 4];
+        const float a1 = XT::to_f32((uint16_t)(v[e] >> 16)) / sv[it][e / 2][(2 * e) % 4 + 1];
+        v[e] = (uint32_t)XT::from_f32(a0) | ((uint32_t)XT::from_f32(a1) << 16);
+      }
+    }
+    // unconditional (the region is padded to PASSES * threads units): a
+    // conditional store would let the compiler sink the load behind the codes
+    reinterpret_cast<u32x4_t*>(xsh)[i] = v;
+  }
+  __syncthreads();
+
+  // This lane's 32 activations and their sums (lanes past the row end: 0).
   const uint32_t ones2 = XT::kMagic2 == F16::kMagic2 ? 0x3C003C00u : 0x3F803F80u;
+  uint32_t xr[16];
+  XSums xs;
+  xs.part[0] = 0.0f;
+  xs.part[1] = 0.0f;
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = i * team + p;
-    if (c < cpr) {
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + 32 * c);
+  for (int q = 0; q < 4; ++q) {
+    const u32x4_t v = reinterpret_cast<const u32x4_t*>(xsh)[4 * c + q];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4_t v = src[q];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) xr[i][4 * q + e] = v[e];
-      }
-      if (SCALE) {
-        const float4_t* sp = reinterpret_cast<const float4_t*>(s + 32 * c);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float4_t sv = sp[q];
-#pragma unroll
-          for (int e = 0; e < 4; e += 2) {
-            const uint32_t pr = xr[i][2 * q + e / 2];
-            const float a0 = XT::to_f32((uint16_t)(pr & 0xFFFFu)) / sv[e];
-            const float a1 = XT::to_f32((uint16_t)(pr >> 16)) / sv[e + 1];
-            xr[i][2 * q + e / 2] = (uint32_t)XT::from_f32(a0) | ((uint32_t)XT::from_f32(a1) << 16);
-          }
-        }
-      }
-      float t = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) t = XT::dot2(xr[i][q], ones2, t);
-      xsum[i] = t;
-    } else {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) xr[i][q] = 0u;
-      xsum[i] = 0.0f;
+    for (int e = 0; e < 4; ++e) {
+      xr[4 * q + e] = live ? v[e] : 0u;
+      xs.part[e & 1] = XT::dot2(xr[4 * q + e], ones2, xs.part[e & 1]);
     }
   }
 
+  const uint32_t magic = vgpr_const(XT::kMagic2);
   const float zsym = (float)(1 << (BITS - 1));
-  for (int row0 = wave * rps * ROWS; row0 < N; row0 += waves * rps * ROWS) {
-    ChunkCodes<BITS> cc[ROWS][CPL];
-    float sc[ROWS][CPL], zc[ROWS][CPL];
-    // Issue every load of the ROWS rows before any arithmetic.
 #pragma unroll
-    for (int rr = 0; rr < ROWS; ++rr) {
-      const int n = row0 + rr * rps + r;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = i * team + p;
-        if (n < N && c < cpr) {
-          load_codes<BITS>(packed, n, K, c, cc[rr][i]);
-          const int64_t gi = (int64_t)n * gpr + (32 * c) / G;
-          sc[rr][i] = half_bits_to_f32(scales[gi]);
-          zc[rr][i] = ASYM ? half_bits_to_f32(zeros[gi]) : zsym;
-        } else {
-#pragma unroll
-          for (int j = 0; j < (BITS == 4 ? 4 : 3); ++j) cc[rr][i].w[j] = 0u;
-          sc[rr][i] = 0.0f;
-          zc[rr][i] = 0.0f;
-        }
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < ROWS; ++rr) {
-      const int n = row0 + rr * rps + r;
-      float acc = 0.0f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const float a = chunk_dot<BITS, XT>(cc[rr][i], xr[i]);
-        acc += sc[rr][i] * (a - (XT::kMagic + zc[rr][i]) * xsum[i]);
-      }
-      acc = team_sum(acc, team);
-      if (p == 0 && n < N) y[n] = XT::from_f32(acc);
-    }
+  for (int st = 0; st < STEPS; ++st) {
+    if (st + kPrefetch < STEPS) issue(st + kPrefetch);
+    const float S = half_bits_to_f32(L[st].s16);
+    const float Z = ASYM ? half_bits_to_f32(L[st].z16) : zsym;
+    part[(st * waves + wave) * 64 + lane] = S * chunk_dot<BITS, XT>(L[st].c, xr, xs, Z, magic);
+  }
+  __syncthreads();
+
+  // Output o = (step, row slot): the spr * 64 partials of one row.
+  for (int o = wave; o < STEPS * rpb; o += waves) {
+    const int st = o / rpb, r = o - st * rpb;
+    float v = 0.0f;
+    for (int g = 0; g < spr; ++g) v += part[(st * waves + r * spr + g) * 64 + lane];
+    v = wave_sum_lane63(v);
+    const int n = row_first - rr + r + st * row_step;
+    if (lane == 63 && n < N) y[n] = XT::from_f32(v);
   }
 }
 
-template <int BITS, bool ASYM, class XT, int CPL, bool SCALE>
-hipError_t launch_cpl(const void* x, const float* s, const void* packed, const void* scales, const void* zeros,
-                      int64_t N, int64_t K, int G, int team_log2, void* y, hipStream_t stream) {
-  constexpr int ROWS = 2;
-  const int rps = 64 >> team_log2;
-  const int64_t waves_needed = (N + (int64_t)rps * ROWS - 1) / ((int64_t)rps * ROWS);
-  int64_t blocks = (waves_needed + kWaves - 1) / kWaves;
-  if (blocks > 65535) blocks = 65535;
-  hipLaunchKernelGGL((gemv_kernel<BITS, ASYM, XT, CPL, SCALE, ROWS>), dim3((unsigned)blocks), dim3(kThreads), 0,
+template <int BITS, bool ASYM, class XT, bool SCALE, int STEPS, int SPR_T, int PASSES>
+hipError_t launch_kernel(const void* x, const float* s, const void* packed, const void* scales, const void* zeros,
+                         int64_t N, int64_t K, int G, int spr, int rpb, int64_t blocks, void* y,
+                         hipStream_t stream) {
+  const int threads = rpb * spr * 64;
+  const size_t lds = (size_t)PASSES * threads * 16 + (size_t)STEPS * (threads / 64) * 64 * 4;
+  hipLaunchKernelGGL((gemv_kernel<BITS, ASYM, XT, SCALE, STEPS, SPR_T, PASSES>), dim3((unsigned)blocks), dim3(threads), lds,
                      stream, static_cast<const uint16_t*>(x), s, static_cast<const uint8_t*>(packed),
-                     static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)N, (int)K, G,
-                     team_log2, static_cast<uint16_t*>(y));
+                     static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)N, (int)K, G, spr,
+                     rpb, static_cast<uint16_t*>(y));
   return hipGetLastError();
+}
+
+template <int BITS, bool ASYM, class XT, bool SCALE, int STEPS>
+hipError_t launch_steps(const void* x, const float* s, const void* packed, const void* scales, const void* zeros,
+                        int64_t N, int64_t K, int G, int spr, int rpb, int64_t blocks, void* y, hipStream_t stream) {
+#define WOQ_FIXED(SPR, PASSES)                                                                                    \
+  if (G == 128 && K == 2048 * SPR)                                                                                \
+    return launch_kernel<BITS, ASYM, XT, SCALE, STEPS, SPR, PASSES>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, \
+                                                             y, stream);
+  WOQ_FIXED(1, 1)
+  WOQ_FIXED(2, 1)
+  WOQ_FIXED(4, 2)
+  WOQ_FIXED(8, 4)
+#undef WOQ_FIXED
+  // General shapes: x staging covers K/8 units in at most 4 passes (K/8 <= 256
+  // spr and the workgroup has at least 64 spr threads).
+  return launch_kernel<BITS, ASYM, XT, SCALE, STEPS, 0, 4>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, y,
+                                                    stream);
 }
 
 template <int BITS, bool ASYM, class XT, bool SCALE>
 hipError_t launch_scale(const void* x, const float* s, const void* packed, const void* scales, const void* zeros,
-                        int64_t N, int64_t K, int G, void* y, hipStream_t stream) {
-  const int cpr = (int)(K / 32);
-  int team_log2 = 0;
-  while ((1 << team_log2) < cpr && team_log2 < 6) ++team_log2;
-  const int team = 1 << team_log2;
-  const int cpl = (cpr + team - 1) / team;
-#define WOQ_CPL_CASE(C) \
-  case C:               \
-    return launch_cpl<BITS, ASYM, XT, C, SCALE>(x, s, packed, scales, zeros, N, K, G, team_log2, y, stream);
-  switch (cpl) {
-    WOQ_CPL_CASE(1)
-    WOQ_CPL_CASE(2)
-    WOQ_CPL_CASE(3)
-    WOQ_CPL_CASE(4)
-    WOQ_CPL_CASE(5)
-    WOQ_CPL_CASE(6)
-    WOQ_CPL_CASE(7)
-    WOQ_CPL_CASE(8)
+                     int64_t N, int64_t K, int G, void* y, hipStream_t stream) {
+  const int64_t cpr = K / 32;
+  const int spr = (int)((cpr + 63) / 64);
+  if (spr > kMaxSegments) return hipErrorInvalidValue;
+  const int rpb = spr >= kTargetWaves ? 1 : kTargetWaves / spr;
+  const int64_t groups = (N + rpb - 1) / rpb;
+  int steps = 1;
+  while (steps < 4 && groups / (2 * steps) >= kTargetBlocks) steps *= 2;
+  const int64_t blocks = (groups + steps - 1) / steps;
+  switch (steps) {
+    case 1:
+      return launch_steps<BITS, ASYM, XT, SCALE, 1>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, y, stream);
+    case 2:
+      return launch_steps<BITS, ASYM, XT, SCALE, 2>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, y, stream);
     default:
-      return hipErrorInvalidValue;
+      return launch_steps<BITS, ASYM, XT, SCALE, 4>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, y, stream);
   }
-#undef WOQ_CPL_CASE
 }
 
 template <int BITS, bool ASYM, class XT>
@@ -224,8 +333,8 @@ hipError_t launch_asym(const void* x, int xdtype, const float* s, const void* pa
 
 }  // namespace
 
-// Largest K the register-resident GEMV handles (8 chunks of 32 per lane).
-int gemv_max_k() { return 64 * 8 * 32; }
+// Largest K the register-resident GEMV handles (8 segments of 64 chunks).
+int gemv_max_k() { return kMaxSegments * 64 * 32; }
 
 hipError_t launch_gemv(const void* x, int xdtype, const float* act_scale, const void* packed, const void* scales,
                        const void* zeros, int64_t N, int64_t K, int bits, int group_size, bool asymmetric, void* y,

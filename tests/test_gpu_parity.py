@@ -212,6 +212,11 @@ def test_gemv_llama_linears_with_awq(i, bits):
     gemv_case(synth.c3_linear(i), bits, True)
 
 
+@pytest.mark.parametrize("i", range(7))
+def test_gemv_llama_linears_with_awq_bf16(i):
+    gemv_case(synth.c3_linear(i), 4, True, "bf16")
+
+
 @pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (67, 160), (129, 640), (33, 2048 + 128), (250, 8192 + 512),
                                  (17, 16384), (5, 20480)])
 def test_gemv_ragged_shapes(N, K):
@@ -305,6 +310,13 @@ def test_gemm_awq_scale():
     gemm_case(lin.W[:300], X, "f16", 4, True, s=lin.act_scale, label="awq")
 
 
+@pytest.mark.parametrize("M", [8, 64])
+def test_gemm_awq_scale_bf16(M):
+    lin = synth.c3_linear(6)
+    X = synth.to_bf16_bits(synth.activations_f32(M, lin.K, 78, lin.extra["channels"]))
+    gemm_case(lin.W[:300], X, "bf16", 4, True, s=lin.act_scale, label="awq-bf16")
+
+
 def test_gemm_one_hot_rows():
     rng = np.random.default_rng(5)
     N, K = 64, 512
@@ -320,6 +332,43 @@ def test_gemm_one_hot_rows():
         w_hat16 = O.dequantize(q).astype(np.float16)
         for m, k in enumerate(ks):
             assert np.array_equal(Y[m].view(np.uint16), w_hat16[:, k].view(np.uint16)), (bits, k)
+
+
+# Large M (>= 128) takes the LDS-staged MFMA kernel: ragged M and N tiles,
+# groups that do not divide its K block, AWQ scales, and for fp16 the
+# fallback to the direct kernel when K % 64 != 0.
+@pytest.mark.parametrize("xdtype", ["f16", "bf16"])
+@pytest.mark.parametrize("bits,asym,G,K,awq", [
+    (4, True, 128, 1536, False), (4, False, 128, 1536, False), (3, True, 128, 1536, False),
+    (3, False, 96, 1536, False), (4, True, 32, 1536, False), (4, True, 32, 1056, False),
+    (3, True, 32, 1056, False), (4, True, 128, 1536, True), (3, True, 64, 1536, True)])
+def test_gemm_large_m_tiles(xdtype, bits, asym, G, K, awq):
+    rng = np.random.default_rng(K + G + bits)
+    M, N = 300, 520
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X32 = rng.standard_normal((M, K)).astype(np.float32)
+    s = None
+    if awq:
+        s = np.exp(rng.uniform(-1.0, 1.0, K)).astype(np.float32)
+        X32[:, rng.choice(K, 8, replace=False)] *= 20.0
+    X = X32.astype(np.float16) if xdtype == "f16" else synth.to_bf16_bits(X32)
+    gemm_case(W, X, xdtype, bits, asym, G=G, s=s, label="large-M")
+
+
+def test_gemm_large_m_one_hot_rows_f16():
+    # fp16 large-M path: w_hat is rounded once to fp16, so a one-hot row of X
+    # returns that rounding bit for bit.
+    rng = np.random.default_rng(9)
+    N, K, M = 320, 1024, 256
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    ks = rng.choice(K, M, replace=True)
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), ks] = 1.0
+    for bits in (3, 4):
+        packed, scales, zeros = ops.quantize_pack(gpu_f16(W), bits, 128, True)
+        Y = ops.gemm(gpu_f16(X), packed, scales, zeros, N, K, bits, 128).cpu().numpy()
+        w_hat16 = O.dequantize(O.quantize(W, bits, 128, True)).astype(np.float16)
+        assert np.array_equal(Y.view(np.uint16), w_hat16[:, ks].T.view(np.uint16)), bits
 
 
 @pytest.mark.parametrize("M", [4, 16, 64])

@@ -93,7 +93,11 @@ __global__ __launch_bounds__(kThreads) void gemm_direct_kernel(
   constexpr int BN = 4 * 16 * NT;
   constexpr int XP = KB + 8;  // LDS row pitch in halves (16 B pad against bank conflicts)
   constexpr int SEG = KB / 8; // 16-byte segments per staged row
+  // bf16 with an AWQ scale: x / s is staged as a bf16 pair hi + lo (about 16
+  // significant bits) and each MFMA is issued for both halves.
+  constexpr bool kSplitX = SCALE && XT::kMagic2 == BF16::kMagic2;
   __shared__ __attribute__((aligned(16))) uint16_t xs[BM * XP];
+  __shared__ __attribute__((aligned(16))) uint16_t xl[kSplitX ? BM * XP : 8];
   __shared__ float xsum_s[BM];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void gemm_direct_kernel(
     __syncthreads();  // previous block's LDS readers are done
     for (int it = threadIdx.x; it < BM * SEG; it += kThreads) {
       const int m = it / SEG, seg = it - m * SEG;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u}, vl = v;
       if (m0 + m < M) v = *reinterpret_cast<const u32x4_t*>(X + (int64_t)(m0 + m) * K + kb + 8 * seg);
       if (SCALE) {
         const float4_t s0 = *reinterpret_cast<const float4_t*>(s + kb + 8 * seg);
@@ -142,13 +146,21 @@ __global__ __launch_bounds__(kThreads) void gemm_direct_kernel(
           const float d1 = e < 2 ? s0[2 * e + 1] : s1[2 * e - 3];
           const float a0 = XT::to_f32((uint16_t)(v[e] & 0xFFFFu)) / d0;
           const float a1 = XT::to_f32((uint16_t)(v[e] >> 16)) / d1;
-          v[e] = (uint32_t)XT::from_f32(a0) | ((uint32_t)XT::from_f32(a1) << 16);
+          const uint16_t h0 = XT::from_f32(a0), h1 = XT::from_f32(a1);
+          v[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          if (kSplitX)
+            vl[e] = (uint32_t)XT::from_f32(a0 - XT::to_f32(h0)) | ((uint32_t)XT::from_f32(a1 - XT::to_f32(h1)) << 16);
         }
       }
       *reinterpret_cast<u32x4_t*>(&xs[m * XP + 8 * seg]) = v;
+      if (kSplitX) *reinterpret_cast<u32x4_t*>(&xl[m * XP + 8 * seg]) = vl;
       float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) ps = XT::dot2(v[e], ones2, ps);
+      if (kSplitX) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ps = XT::dot2(vl[e], ones2, ps);
+      }
       ps = team_sum(ps, SEG);
       if (seg == 0) xsum_s[m] = ps;
     }
@@ -157,15 +169,21 @@ __global__ __launch_bounds__(kThreads) void gemm_direct_kernel(
     const int t0 = BITS == 3 ? ((kbeg & 31) >> 1) : 0;
 #pragma unroll
     for (int q = 0; q < KB / 32; ++q) {
-      u32x4_t a[MT];
+      u32x4_t a[MT], al[kSplitX ? MT : 1];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
         a[mt] = *reinterpret_cast<const u32x4_t*>(&xs[(16 * mt + lr) * XP + lg * (KB / 4) + 8 * q]);
+        if constexpr (kSplitX)
+          al[mt] = *reinterpret_cast<const u32x4_t*>(&xl[(16 * mt + lr) * XP + lg * (KB / 4) + 8 * q]);
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const u32x4_t b = b_fragment<BITS, KB, XT>(bc[nt], q, t0);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) part[mt][nt] = XT::mfma16x16x32(a[mt], b, part[mt][nt]);
+        for (int mt = 0; mt < MT; ++mt) {
+          part[mt][nt] = XT::mfma16x16x32(a[mt], b, part[mt][nt]);
+          if constexpr (kSplitX) part[mt][nt] = XT::mfma16x16x32(al[mt], b, part[mt][nt]);
+        }
       }
     }
 #pragma unroll
@@ -256,9 +274,17 @@ hipError_t launch_asym(const void* X, int xdtype, const float* s, const void* pa
 
 }  // namespace
 
+// Rows of X from which the LDS-staged MFMA kernel (one dequantization per
+// 256 x 256 tile) replaces the direct-decode kernel; its fp16 variant steps K
+// by 64.
+constexpr int64_t kLdsGemmMinM = 128;
+
 hipError_t launch_gemm(const void* X, int xdtype, const float* act_scale, const void* packed, const void* scales,
                        const void* zeros, int64_t M, int64_t N, int64_t K, int bits, int group_size, bool asymmetric,
                        void* Y, hipStream_t stream) {
+  if (M >= kLdsGemmMinM && (xdtype != 0 || K % 64 == 0))
+    return launch_gemm_lds(X, xdtype, act_scale, packed, scales, zeros, M, N, K, bits, group_size, asymmetric, Y,
+                           stream);
   if (bits == 4)
     return asymmetric
                ? launch_asym<4, true>(X, xdtype, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream)

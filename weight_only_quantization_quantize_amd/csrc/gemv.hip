@@ -11,7 +11,8 @@
 // 32 weights (one 16-byte / 12-byte load per lane per segment).  A workgroup
 // holds RPB rows x SPR segments, one wave per (row, segment); lane p of the
 // wave for segment g always owns chunk 64 g + p, so its 32 activations are
-// read once (from x / s staged in LDS) and stay in 16 registers.
+// read once (from x / s staged in LDS) and stay in 16 registers (32 for bf16
+// with an AWQ scale, where x / s is kept as a bf16 pair hi + lo).
 //
 // Order of the stream.  Workgroup b handles the row groups b, b + B, b + 2B,
 // ... (B = number of workgroups), so at every step the whole GPU reads one
@@ -157,6 +158,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
                                                     int spr_rt, int rpb_rt, uint16_t* __restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   constexpr bool kFixed = SPR_T > 0;
+  // bf16 with an AWQ scale: x / s is staged as a bf16 pair hi + lo (about 16
+  // significant bits, a second x region in LDS) and each chunk is dotted with
+  // both halves.
+  constexpr bool kSplitX = SCALE && XT::kMagic2 == BF16::kMagic2;
   const int K = kFixed ? 2048 * SPR_T : K_rt;
   const int G = kFixed ? 128 : G_rt;
   const int spr = kFixed ? SPR_T : spr_rt;
@@ -164,7 +169,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
   const int nthreads = kFixed ? rpb * spr * 64 : (int)blockDim.x;
   const int cpr = K >> 5;  // chunks per row
   uint32_t* xsh = lds;
-  float* part = reinterpret_cast<float*>(lds + PASSES * nthreads * 4);
+  uint32_t* xlo = lds + PASSES * nthreads * 4;  // kSplitX only
+  float* part = reinterpret_cast<float*>(lds + (kSplitX ? 2 : 1) * PASSES * nthreads * 4);
   const int waves = nthreads >> 6;
   const int lane = threadIdx.x & 63;
   // wave-uniform values live in scalar registers
@@ -212,27 +218,30 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
 #pragma unroll
   for (int it = 0; it < PASSES; ++it) {
     const int i = threadIdx.x + it * nthreads;
-    u32x4_t v = xv[it];
+    u32x4_t v = xv[it], vl = u32x4_t{0u, 0u, 0u, 0u};
     if (SCALE) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float a0 = XT::to_f32((uint16_t)(v[e] & 0xFFFFu)) / sv[it][e / 2][(2 * e) % 4];
         const float a1 = XT::to_f32((uint16_t)(v[e] >> 16)) / sv[it][e / 2][(2 * e) % 4 + 1];
-        v[e] = (uint32_t)XT::from_f32(a0) | ((uint32_t)XT::from_f32(a1) << 16);
+        const uint16_t h0 = XT::from_f32(a0), h1 = XT::from_f32(a1);
+        v[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        if (kSplitX)
+          vl[e] = (uint32_t)XT::from_f32(a0 - XT::to_f32(h0)) | ((uint32_t)XT::from_f32(a1 - XT::to_f32(h1)) << 16);
       }
     }
     // unconditional (the region is padded to PASSES * threads units): a
     // conditional store would let the compiler sink the load behind the codes
     reinterpret_cast<u32x4_t*>(xsh)[i] = v;
+    if (kSplitX) reinterpret_cast<u32x4_t*>(xlo)[i] = vl;
   }
   __syncthreads();
 
   // This lane's 32 activations and their sums (lanes past the row end: 0).
   const uint32_t ones2 = XT::kMagic2 == F16::kMagic2 ? 0x3C003C00u : 0x3F803F80u;
-  uint32_t xr[16];
-  XSums xs;
-  xs.part[0] = 0.0f;
-  xs.part[1] = 0.0f;
+  uint32_t xr[16], xl[kSplitX ? 16 : 1];
+  XSums xs, xsl;
+  xs.part[0] = xs.part[1] = xsl.part[0] = xsl.part[1] = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const u32x4_t v = reinterpret_cast<const u32x4_t*>(xsh)[4 * c + q];
@@ -240,6 +249,14 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
     for (int e = 0; e < 4; ++e) {
       xr[4 * q + e] = live ? v[e] : 0u;
       xs.part[e & 1] = XT::dot2(xr[4 * q + e], ones2, xs.part[e & 1]);
+    }
+    if constexpr (kSplitX) {
+      const u32x4_t vl = reinterpret_cast<const u32x4_t*>(xlo)[4 * c + q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xl[4 * q + e] = live ? vl[e] : 0u;
+        xsl.part[e & 1] = XT::dot2(xl[4 * q + e], ones2, xsl.part[e & 1]);
+      }
     }
   }
 
@@ -250,7 +267,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
     if (st + kPrefetch < STEPS) issue(st + kPrefetch);
     const float S = half_bits_to_f32(L[st].s16);
     const float Z = ASYM ? half_bits_to_f32(L[st].z16) : zsym;
-    part[(st * waves + wave) * 64 + lane] = S * chunk_dot<BITS, XT>(L[st].c, xr, xs, Z, magic);
+    float d = chunk_dot<BITS, XT>(L[st].c, xr, xs, Z, magic);
+    if constexpr (kSplitX) d += chunk_dot<BITS, XT>(L[st].c, xl, xsl, Z, magic);
+    part[(st * waves + wave) * 64 + lane] = S * d;
   }
   __syncthreads();
 
@@ -270,7 +289,8 @@ hipError_t launch_kernel(const void* x, const float* s, const void* packed, cons
                          int64_t N, int64_t K, int G, int spr, int rpb, int64_t blocks, void* y,
                          hipStream_t stream) {
   const int threads = rpb * spr * 64;
-  const size_t lds = (size_t)PASSES * threads * 16 + (size_t)STEPS * (threads / 64) * 64 * 4;
+  constexpr bool kSplitX = SCALE && XT::kMagic2 == BF16::kMagic2;
+  const size_t lds = (size_t)(kSplitX ? 2 : 1) * PASSES * threads * 16 + (size_t)STEPS * (threads / 64) * 64 * 4;
   hipLaunchKernelGGL((gemv_kernel<BITS, ASYM, XT, SCALE, STEPS, SPR_T, PASSES>), dim3((unsigned)blocks), dim3(threads), lds,
                      stream, static_cast<const uint16_t*>(x), s, static_cast<const uint8_t*>(packed),
                      static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)N, (int)K, G, spr,

@@ -16,7 +16,18 @@ kernel before the timed steps so host-side launch latency never shows up as
 GPU idle time inside the events.  The CPU oracle is timed on a bounded sample
 of the same workload (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--variants] [--extra FILE]
+The same run also times the other rows of the path on their own workloads
+(`rows`): the LLaMA-2-7B-shaped decode GEMVs with AWQ scales, the small-batch
+GEMM (M = 4, 16, 64; K = 8192, N = 28672), the prefill GEMM (M = 2048,
+K = 4096, N = 11008) and quantize_pack over 32 layers of the LLaMA-2-7B linear
+shapes, each as back-to-back launches over rotated weight sets with its
+roofline fraction and a sampled check against the oracle.
+
+`--write-traffic DIR` turns the rocprofv3 FETCH_SIZE / WRITE_SIZE CSVs of a
+bench run and of a `--copy-calibration` run (pmc_fetch, pmc_write,
+pmc_copy_fetch, pmc_copy_write under DIR) into profiles/gemv_traffic.json.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--variants] [--no-rows]
 """
 from __future__ import annotations
 
@@ -58,6 +69,10 @@ def parse():
     p.add_argument("--variants", action="store_true", help="also time 4/3-bit x sym/asym GEMV variants")
     p.add_argument("--extra", default=None, help="write per-config results (JSON lines) to this file")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-rows", action="store_true", help="skip the per-row timings of the other workloads")
+    p.add_argument("--write-traffic", default=None, metavar="DIR",
+                   help="write profiles/gemv_traffic.json from rocprofv3 counter CSVs in DIR and exit")
+    p.add_argument("--copy-mib", type=int, default=256, help="size of the --copy-calibration run used for DIR")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (for HBM counter calibration) and exit")
     return p.parse_args()
@@ -100,6 +115,200 @@ def measured_traffic():
         if hashlib.sha256(f.read()).hexdigest() != t.get("kernel_source_sha256"):
             return None
     return int(t["bytes_per_launch"])
+
+
+def write_traffic(prof_dir, copy_mib):
+    """Scale the GEMV's FETCH_SIZE / WRITE_SIZE (KiB per dispatch, median) by
+    what the same counters read for a plain device copy of copy_mib MiB."""
+    import csv
+    import hashlib
+
+    def per_kernel(name):
+        d = {}
+        with open(os.path.join(prof_dir, f"{name}_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                d.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return d
+
+    def copy_kib(d):
+        v = [x for k, xs in d.items() if "copyBuffer" in k for x in xs]
+        if len(v) != 1:
+            raise SystemExit(f"expected one copy dispatch in the calibration run, found {len(v)}")
+        return v[0]
+
+    fetch_scale = copy_mib * 1024 / copy_kib(per_kernel("pmc_copy_fetch"))
+    write_scale = copy_mib * 1024 / copy_kib(per_kernel("pmc_copy_write"))
+    fetch, write = per_kernel("pmc_fetch"), per_kernel("pmc_write")
+    table = []
+    for k in sorted(fetch):
+        if "woq::" not in k:
+            continue
+        fk, wk = float(np.median(fetch[k])), float(np.median(write.get(k, [0.0])))
+        table.append((k, len(fetch[k]), fk, wk, fk * fetch_scale * 1024, wk * write_scale * 1024))
+    gemv = [t for t in table if "gemv_kernel<4, true, woq::F16, false, 4, 4, 2>" in t[0]]
+    if len(gemv) != 1:
+        raise SystemExit("the c2 GEMV kernel is not in the counter CSVs")
+    k, _, fk, wk, rb, wb = gemv[0]
+    with open(os.path.join(ROOT, "weight_only_quantization_quantize_amd", "csrc", "gemv.hip"), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    out = {
+        "kernel": "gemv_kernel<4, true, F16, false, 4, 4, 2>",
+        "workload": "M=1 K=8192 N=8192 4-bit asym g128",
+        "kernel_source_sha256": sha,
+        "fetch_size_kib": fk,
+        "write_size_kib": wk,
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "bytes_per_launch": int(round(rb + wb)),
+        "summary": "profiles/gemv_w4a16_g128_m1_k8192_n8192.md",
+    }
+    with open(os.path.join(ROOT, "profiles", "gemv_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"fetch scale {fetch_scale:.4f}, write scale {write_scale:.4f}")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |")
+    print("|---|---|---|---|---|---|")
+    for k, n, fk, wk, rb, wb in table:
+        name = k.replace("void ", "").replace("woq::(anonymous namespace)::", "").replace("woq::", "").split("(")[0]
+        print(f"| {name} | {n} | {fk:.1f} | {wk:.1f} | "
+              f"{rb / 1e6:.3f} | {wb / 1e6:.3f} |")
+    print(json.dumps(out))
+
+
+def burst_us(torch, launches, reps=3):
+    """Average duration (us) of each launch when the callables in `launches`
+    run back to back behind a queue prefill, HIP events on the launch stream;
+    the best of `reps` bursts."""
+    best = None
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(PREFILL_CYCLES // 4)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for f in launches:
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / len(launches)
+        best = us if best is None else min(best, us)
+    return best
+
+
+def time_rows(torch, ops, synth):
+    """Per-row timings on the other workloads, each with a sampled oracle check."""
+    from oracle import woq_oracle as O
+
+    dev = torch.device("cuda:0")
+    rows = {}
+
+    def x_tensor(X, xdtype):
+        if xdtype == "f16":
+            return torch.from_numpy(X).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(X).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def host_y(Y):
+        if Y.dtype == torch.bfloat16:
+            return O.bf16_bits_to_f64(Y.view(torch.int16).cpu().numpy().view(np.uint16))
+        return Y.cpu().numpy().astype(np.float64)
+
+    def sampled_rel_l2(lin, Y, s, sel):
+        _, _, _, q = O.quantize_pack(lin.W[sel], 4, 128, True, s)
+        ref = O.gemm(O.activations_f64(lin.X, lin.xdtype), O.dequantize(q), s)
+        return O.rel_l2(host_y(Y)[:, sel], ref)
+
+    # Decode GEMVs of the LLaMA-2-7B linears with their AWQ scales (4-bit asym g128).
+    c3 = {}
+    for i in range(7):
+        lin = synth.c3_linear(i)
+        W = torch.from_numpy(lin.W).to(dev)
+        s = torch.from_numpy(lin.act_scale).to(dev)
+        x = torch.from_numpy(lin.X[0]).to(dev)
+        nb = gemv_bytes(lin.N, lin.K, 4, 128, True, act_scale=True)
+        R = rotate_count(nb)
+        sets = [ops.quantize_pack(W, 4, 128, True, s) for _ in range(R)]
+        y = torch.empty(lin.N, dtype=torch.float16, device=dev)
+        us = burst_us(torch, [lambda j=j: ops.gemv(x, *sets[j % R], lin.N, lin.K, 4, 128, s, out=y)
+                              for j in range(10 * R)])
+        sel = np.arange(0, lin.N, max(1, lin.N // 256))
+        err = sampled_rel_l2(lin, y[None, :], lin.act_scale, sel)
+        c3[lin.name] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
+                        "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": nb,
+                        "rel_l2_sampled": float(f"{err:.3g}")}
+        del sets, W
+    rows["c3_decode_gemv_awq"] = c3
+
+    # Small-batch GEMM, M = 4 / 16 / 64, K = 8192, N = 28672.
+    c4 = {}
+    W, W_np = None, None
+    for xdtype in ("f16", "bf16"):
+        for M in (4, 16, 64):
+            lin = synth.c4_small_batch(M, xdtype, W=W_np)
+            W_np = lin.W
+            if W is None:
+                W = torch.from_numpy(lin.W).to(dev)
+                nbw = gemv_bytes(lin.N, lin.K, 4, 128, True, M=0)
+                R = rotate_count(nbw)
+                sets = [ops.quantize_pack(W, 4, 128, True) for _ in range(R)]
+            X = x_tensor(lin.X, xdtype)
+            Y = torch.empty(M, lin.N, dtype=X.dtype, device=dev)
+            nb = gemv_bytes(lin.N, lin.K, 4, 128, True, M=M)
+            us = burst_us(torch, [lambda j=j: ops.gemm(X, *sets[j % R], lin.N, lin.K, 4, 128, out=Y)
+                                  for j in range(4 * R)])
+            sel = np.arange(0, lin.N, lin.N // 128)
+            err = sampled_rel_l2(lin, Y, None, sel)
+            c4[f"M{M}_{xdtype}"] = {"us": round(us, 2), "gbs": round(nb / us / 1e3, 1),
+                                    "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+                                    "tflops": round(2 * M * lin.N * lin.K / us / 1e6, 1), "bytes": nb,
+                                    "rel_l2_sampled": float(f"{err:.3g}")}
+    del sets, W
+    rows["c4_small_batch_gemm"] = c4
+
+    # Prefill GEMM, M = 2048, K = 4096, N = 11008.
+    lin = synth.c5_prefill()
+    W = torch.from_numpy(lin.W).to(dev)
+    sets = [ops.quantize_pack(W, 4, 128, True) for _ in range(4)]
+    c5 = {}
+    for xdtype in ("f16", "bf16"):
+        X = torch.from_numpy(lin.X).to(dev)
+        if xdtype == "bf16":
+            X = X.float().to(torch.bfloat16)
+        Y = torch.empty(lin.M, lin.N, dtype=X.dtype, device=dev)
+        us = burst_us(torch, [lambda j=j: ops.gemm(X, *sets[j % 4], lin.N, lin.K, 4, 128, out=Y)
+                              for j in range(12)])
+        fl = 2 * lin.M * lin.N * lin.K
+        entry = {"us": round(us, 1), "tflops": round(fl / us / 1e6, 1),
+                 "frac_mfma": round(fl / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4), "flop": fl}
+        if xdtype == "f16":
+            sel = np.arange(0, lin.N, lin.N // 96)
+            entry["rel_l2_sampled"] = float(f"{sampled_rel_l2(lin, Y, None, sel):.3g}")
+        c5[xdtype] = entry
+    del sets, W
+    rows["c5_prefill_gemm"] = c5
+
+    # quantize_pack over 32 layers of the LLaMA-2-7B linear shapes (weights
+    # generated on the device, seed 5100 + layer), 4-bit asym g128.
+    shapes = [(N, K) for _, N, K in synth.LLAMA7B_LINEARS]
+    total_bytes, total_us = 0, 0.0
+    g = torch.Generator(device=dev)
+    for layer in range(32):
+        g.manual_seed(5100 + layer)
+        Ws = [(torch.randn(N, K, generator=g, device=dev) * 0.02).half() for N, K in shapes]
+        outs = [ops.quantize_pack(w, 4, 128, True) for w in Ws]
+        total_us += burst_us(torch, [lambda w=w, o=o: ops.quantize_pack(w, 4, 128, True, out=o)
+                                     for w, o in zip(Ws, outs)], reps=1) * len(Ws)
+        total_bytes += sum(quantize_pack_bytes(N, K, 4, 128, True) for N, K in shapes)
+        if layer == 0:
+            w0 = Ws[0].cpu().numpy()
+            rp, rs, rz, _ = O.quantize_pack(w0[:256], 4, 128, True)
+            qp_equal = bool(np.array_equal(outs[0][0][:256].cpu().numpy(), rp)
+                            and np.array_equal(outs[0][1][:256].cpu().numpy().view(np.uint16), rs.view(np.uint16))
+                            and np.array_equal(outs[0][2][:256].cpu().numpy().view(np.uint16), rz.view(np.uint16)))
+        del Ws, outs
+    rows["quantize_pack_32_layers"] = {"ms": round(total_us / 1e3, 3), "bytes": total_bytes,
+                                       "gbs": round(total_bytes / total_us / 1e3, 1),
+                                       "frac_hbm": round(total_bytes / total_us / 1e3 / HBM_PEAK_GBS, 4),
+                                       "sampled_bytes_equal": qp_equal}
+    return rows
 
 
 def rotate_count(bytes_per_set, minimum=4):
@@ -173,6 +382,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is not sharded "
               "across GPUs in this build)", file=sys.stderr)
         sys.exit(2)
+
+    if args.write_traffic:
+        write_traffic(args.write_traffic, args.copy_mib)
+        return
 
     import torch
 
@@ -291,6 +504,10 @@ def main():
                 "gemv_us": round(ms * 1e3, 3), "gbs": round(vb / (ms * 1e-3) / 1e9, 1),
                 "pct_hbm_peak": round(100 * vb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2), "bytes": vb}
         result["variants"] = var
+
+    if not args.no_rows:
+        del Ws, W0
+        result["rows"] = time_rows(torch, ops, synth)
 
     if not args.no_cpu_baseline:
         ops.gemv(x, *sets[0], N, K, bits, G, out=y)

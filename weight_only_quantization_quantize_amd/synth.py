@@ -165,10 +165,13 @@ def c3_linear(i: int, with_weights: bool = True) -> Linear:
     return Linear(f"c3_{name}_1x{K}x{N}", 1, N, K, W, to_f16(x32), "f16", s, {"channels": ch})
 
 
-def c4_small_batch(M: int, xdtype: str = "f16", N: int = 28672, K: int = 8192) -> Linear:
+def c4_small_batch(M: int, xdtype: str = "f16", N: int = 28672, K: int = 8192,
+                   W: Optional[np.ndarray] = None) -> Linear:
     """Small-batch GEMM, M in {4, 16, 64}, K=8192, N=28672: W ~ N(0,0.02)
-    (seed 4001), X ~ N(0,1) (seed 4002) stored as fp16 or bf16."""
-    return Linear(f"c4_{M}x{K}x{N}_{xdtype}", M, N, K, weights(N, K, 4001), activations(M, K, 4002, xdtype), xdtype)
+    (seed 4001; pass a previous call's W to skip regenerating it), X ~ N(0,1)
+    (seed 4002) stored as fp16 or bf16."""
+    W = weights(N, K, 4001) if W is None else W
+    return Linear(f"c4_{M}x{K}x{N}_{xdtype}", M, N, K, W, activations(M, K, 4002, xdtype), xdtype)
 
 
 def c5_prefill(M: int = 2048, N: int = 11008, K: int = 4096) -> Linear:

@@ -274,9 +274,8 @@ hipError_t launch_asym(const void* X, int xdtype, const float* s, const void* pa
 
 }  // namespace
 
-// Rows of X from which the LDS-staged MFMA kernel (one dequantization per
-// 256 x 256 tile) replaces the direct-decode kernel; its fp16 variant steps K
-// by 64.
+// Rows of X from which the LDS-staged MFMA kernel replaces the direct-decode
+// kernel; its fp16 variant steps K by 64.
 constexpr int64_t kLdsGemmMinM = 128;
 
 hipError_t launch_gemm(const void* X, int xdtype, const float* act_scale, const void* packed, const void* scales,

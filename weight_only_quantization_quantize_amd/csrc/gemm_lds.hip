@@ -23,9 +23,9 @@
 // hi), and each K step issues the MFMAs twice (X hi + X lo): the weight error
 // drops from 2^-9 to about 2^-17 relative, at twice the MFMA work of fp16.
 //
-// The global loads of block k + 1 are issued before block k's MFMAs and
-// written to the other LDS stage after them, so one barrier per block
-// suffices.  Tiles are assigned so that each of the 8 XCDs works on a
+// X is loaded two blocks ahead and the packed codes kPB blocks ahead, each in
+// a ring of registers; block k + 1 is written to the other LDS stage after
+// block k's MFMAs, so one barrier per block suffices.  Tiles are assigned so that each of the 8 XCDs works on a
 // contiguous range of the tile grid with the N tile index fastest: the
 // 256-row X tile a range shares stays in that XCD's L2.
 //
@@ -105,6 +105,17 @@ __device__ inline uint32_t code_pair(const uint32_t* w, int t, int hi_base) {
   }
 }
 
+#ifndef WOQ_LDS_PB
+#define WOQ_LDS_PB 2
+#endif
+constexpr int kPB = WOQ_LDS_PB;  // blocks of packed codes in flight
+// Blocks of X in flight: 2, except for bf16 with an AWQ scale, whose folded
+// weight path needs the registers.
+template <class XT, bool SCALE>
+constexpr int x_prefetch() {
+  return XT::kMagic2 == BF16::kMagic2 && SCALE ? 1 : 2;
+}
+
 template <int BITS, bool ASYM, class XT, bool SCALE>
 __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ s, const uint8_t* __restrict__ packed,
@@ -131,15 +142,14 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
   const int gpr = K / G;
   const int kblocks = K / BK;
 
-  // A staging: thread t owns segment t % kSegs of rows t / kSegs + i * (512 / kSegs).
+  // A staging: thread t owns segment t % kSegs of rows t / kSegs + i * (512 /
+  // kSegs).  Rows past M read row M - 1; their outputs are never stored.
   constexpr int kRowStep = kThreads / TL::kSegs;
   const int a_seg = tid % TL::kSegs, a_r0 = tid / TL::kSegs;
   const uint16_t* a_src[TL::kAUnits];
-  uint32_t a_live = 0;
 #pragma unroll
   for (int i = 0; i < TL::kAUnits; ++i) {
     const int r = m0 + a_r0 + kRowStep * i;
-    a_live |= (r < M ? 1u : 0u) << i;
     a_src[i] = X + (int64_t)(r < M ? r : M - 1) * K + 8 * a_seg;
   }
   const uint32_t a_dst = (uint32_t)(a_r0 * LD + 8 * a_seg);
@@ -155,15 +165,27 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
   // to 8 significant bits would dominate the error when a few scaled channels
   // carry the output.
   constexpr bool kScaleA = SCALE && !kSplit, kScaleB = SCALE && kSplit;
-  struct Regs {
+  constexpr int kPA = x_prefetch<XT, SCALE>();
+  // X is loaded kPA blocks ahead and the packed codes kPB blocks ahead, each
+  // in a ring of registers.
+  struct ARegs {
     u32x4_t a[TL::kAUnits];
-    uint32_t w[BITS == 4 ? TL::kCodes / 8 : 3];
-    uint16_t s16, z16;
     float4_t sv[kScaleB ? TL::kCodes / 4 : 1];  // s[k] of this thread's codes
   };
-  auto load_block = [&](Regs& R, int kb) {
+  struct BRegs {
+    uint32_t w[BITS == 4 ? TL::kCodes / 8 : 3];
+    uint16_t s16, z16;
+  };
+  auto load_a = [&](ARegs& R, int kb) {
 #pragma unroll
     for (int i = 0; i < TL::kAUnits; ++i) R.a[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + kb);
+    if constexpr (kScaleB) {
+      const int kc = kb + (BK / 2) * b_half;
+#pragma unroll
+      for (int j = 0; j < TL::kCodes / 4; ++j) R.sv[j] = *reinterpret_cast<const float4_t*>(s + kc + 4 * j);
+    }
+  };
+  auto load_b = [&](BRegs& R, int kb) {
     const int kc = kb + (BK / 2) * b_half;  // first K of this thread's codes
     if constexpr (BITS == 4) {
       if constexpr (TL::kCodes == 32) {
@@ -189,12 +211,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
     const int64_t gi = g_row + kc / G;
     R.s16 = scales[gi];
     R.z16 = ASYM ? zeros[gi] : (uint16_t)0;
-    if constexpr (kScaleB) {
-#pragma unroll
-      for (int j = 0; j < TL::kCodes / 4; ++j) R.sv[j] = *reinterpret_cast<const float4_t*>(s + kc + 4 * j);
-    }
   };
-  auto store_block = [&](const Regs& R, int st, int kb) {
+  auto store_block = [&](const ARegs& RA, const BRegs& R, int st, int kb) {
     uint16_t* base = lds + st * kStage;
     float inv[8];
     if constexpr (kScaleA) {
@@ -208,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
     }
 #pragma unroll
     for (int i = 0; i < TL::kAUnits; ++i) {
-      u32x4_t v = (a_live >> i) & 1u ? R.a[i] : u32x4_t{0u, 0u, 0u, 0u};
+      u32x4_t v = RA.a[i];
       if constexpr (kScaleA) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -229,8 +247,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
       for (int t = 0; t < kPairs; ++t) {
         float r0 = 1.0f, r1 = 1.0f;
         if constexpr (kScaleB) {
-          r0 = 1.0f / R.sv[t >> 1][2 * (t & 1)];
-          r1 = 1.0f / R.sv[t >> 1][2 * (t & 1) + 1];
+          r0 = 1.0f / RA.sv[t >> 1][2 * (t & 1)];
+          r1 = 1.0f / RA.sv[t >> 1][2 * (t & 1) + 1];
         }
         dequant_pair_split<kScaleB>(code_pair<BITS>(R.w, t, hi_base), Z, S, r0, r1, hi[t], lo[t]);
       }
@@ -286,19 +304,32 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
     }
   };
 
-  // One register stage and two LDS stages: the loads of block kt + 1 are in
-  // flight while block kt is multiplied, then written to the other stage; one
-  // barrier per block.  The last iteration reloads its own block into the
-  // unused stage, which keeps the loop free of branches.
-  Regs R;
-  load_block(R, 0);
-  store_block(R, 0, 0);
+  // Two LDS stages: while block kt is multiplied, X up to block kt + kPA and
+  // codes up to block kt + kPB are in flight; block kt + 1 is then written to
+  // the other stage; one barrier per block.  Block indices past the end are
+  // clamped to the last block (reloaded, written to the unused stage), which
+  // keeps the loop free of branches.
+  const int last = kblocks - 1;
+  ARegs RA[kPA];
+  BRegs RB[kPB];
+#pragma unroll
+  for (int j = 0; j < kPA; ++j) load_a(RA[j], (j < last ? j : last) * BK);
+#pragma unroll
+  for (int j = 0; j < kPB; ++j) load_b(RB[j], (j < last ? j : last) * BK);
+  store_block(RA[0], RB[0], 0, 0);
   __syncthreads();
   for (int kt = 0; kt < kblocks; ++kt) {
-    const int nxt = kt + 1 < kblocks ? kt + 1 : kt;
-    load_block(R, nxt * BK);
+    const int nxt = kt + 1 < kblocks ? kt + 1 : last;
+    const int far_a = kt + kPA < kblocks ? kt + kPA : last;
+    const int far_b = kt + kPB < kblocks ? kt + kPB : last;
+#pragma unroll
+    for (int j = 0; j + 1 < kPA; ++j) RA[j] = RA[j + 1];
+    load_a(RA[kPA - 1], far_a * BK);
+#pragma unroll
+    for (int j = 0; j + 1 < kPB; ++j) RB[j] = RB[j + 1];
+    load_b(RB[kPB - 1], far_b * BK);
     mma_block(kt & 1);
-    store_block(R, (kt + 1) & 1, nxt * BK);
+    store_block(RA[0], RB[0], (kt + 1) & 1, nxt * BK);
     __syncthreads();
   }
 

@@ -8,18 +8,22 @@
 // caveats).  Here the codes are widened to 16-bit floats and fed to
 // v_mfma_f32_16x16x32_{f16,bf16}.
 //
-// Direct-decode kernel (this file): a workgroup of 4 waves owns a tile of
-// 16*MT rows of X and 4 * 16*NT columns of W.  Per K-block of KB (32, 64 or
+// Direct-decode kernel (this file): a workgroup owns a tile of 16*MT rows of
+// X and 4 * 16*NT columns of W, and splits K between NS slices of 4 waves
+// (their partial sums meet in LDS at the end).  Per K-block of KB (32, 64 or
 // 128, never crossing a group):
-//  * X[m0:m0+16MT, kb:kb+KB] is staged through LDS once for the 4 waves
-//    (divided by the AWQ scale and rounded when one is given), together with
-//    each row's sum over the block;
+//  * X[m0:m0+16MT, kb:kb+KB] is staged through LDS once for a slice's 4 waves
+//    (divided by the AWQ scale and rounded when one is given);
 //  * every lane loads the codes of its own B fragment straight from HBM (one
 //    16-byte load per column tile for KB = 128), turns each code into the
-//    16-bit float MAGIC + u (exact) and issues KB/32 MFMAs per (mt, nt);
+//    16-bit float MAGIC + u (exact, one v_and_or_b32 per pair) and issues
+//    KB/32 MFMAs per (mt, nt), plus one per mt against an all-ones fragment
+//    that sums x over the group in the same layout;
 //  * at the end of a group the fp32 partial sums are corrected and scaled,
 //    acc += S (part - (MAGIC + Z) * sum x), so the only roundings are the
 //    MFMA's fp32 accumulation and the final conversion of Y.
+// Codes and X travel a few blocks ahead in register rings; the scales and
+// zero points of the workgroup's columns are staged in LDS once.
 //
 // MFMA operand slots: lane l of a 16x16x32 MFMA supplies A[m = l%16][slot
 // 8*(l/16) + j] and B[slot 8*(l/16) + j][n = l%16], j = 0..7, and receives
@@ -70,73 +74,160 @@ __device__ inline void load_b(const uint8_t* __restrict__ packed, int64_t n, int
   }
 }
 
-// B fragment (8 consecutive K of one column) for MFMA q of the K-block.
+// B fragment (8 consecutive K of one column) for MFMA q of the K-block;
+// magic2 = MAGIC in both halves, held in a VGPR (one v_and_or_b32 per pair).
 template <int BITS, int KB, class XT>
-__device__ inline u32x4_t b_fragment(const BCodes<BITS, KB>& b, int q, int t0) {
+__device__ inline u32x4_t b_fragment(const BCodes<BITS, KB>& b, int q, int t0, uint32_t magic2) {
   u32x4_t f;
   if (BITS == 4) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) f[t] = pair4(b.w[q], t, XT::kMagic2);
+    for (int t = 0; t < 4; ++t) f[t] = pair4(b.w[q], t, magic2);
   } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) f[t] = pair3(b.w[0], b.w[1], b.w[2], t0 + 4 * q + t, XT::kMagic2);
+    for (int t = 0; t < 4; ++t) f[t] = pair3(b.w[0], b.w[1], b.w[2], t0 + 4 * q + t, magic2);
   }
   return f;
 }
 
-template <int BITS, bool ASYM, class XT, int MT, int NT, int KB, bool SCALE>
-__global__ __launch_bounds__(kThreads) void gemm_direct_kernel(
+// Codes of one K-block for one column tile, with the block's scale and zero
+// point (a K-block never crosses a group).
+template <int BITS, int KB>
+struct BBlock {
+  BCodes<BITS, KB> c;
+  uint16_t s16, z16;
+};
+
+// Scale / zero entries a workgroup can hold in LDS (per array).
+constexpr int kSZLds = 8192;
+
+// NS: K slices per workgroup.  The workgroup is NS groups of 4 waves; slice
+// q runs the K-blocks [q bps, (q + 1) bps) of the same BN columns, and the NS
+// partial results are summed through LDS at the end.  Small M has little
+// work per column, so splitting K is what gives each CU enough waves (and
+// loads in flight) to keep HBM busy.
+template <int BITS, bool ASYM, class XT, int MT, int NT, int KB, bool SCALE, int P, bool SZL, int NS>
+__global__ __launch_bounds__(kThreads * NS) void gemm_direct_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ s, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int M, int N, int K, int G,
     uint16_t* __restrict__ Y) {
   constexpr int BM = 16 * MT;
   constexpr int BN = 4 * 16 * NT;
-  constexpr int XP = KB + 8;  // LDS row pitch in halves (16 B pad against bank conflicts)
-  constexpr int SEG = KB / 8; // 16-byte segments per staged row
+  constexpr int XP = KB + 8;   // LDS row pitch in halves (16 B pad against bank conflicts)
+  constexpr int SEG = KB / 8;  // 16-byte segments per staged row
+  constexpr int UNITS = BM * SEG;
+  constexpr int XU = (UNITS + kThreads - 1) / kThreads;  // X segments per thread of a slice
   // bf16 with an AWQ scale: x / s is staged as a bf16 pair hi + lo (about 16
   // significant bits) and each MFMA is issued for both halves.
   constexpr bool kSplitX = SCALE && XT::kMagic2 == BF16::kMagic2;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[BM * XP];
-  __shared__ __attribute__((aligned(16))) uint16_t xl[kSplitX ? BM * XP : 8];
-  __shared__ float xsum_s[BM];
+  // Two X stages (one barrier per K-block); the codes and X are loaded P
+  // blocks ahead into register rings.
+  __shared__ __attribute__((aligned(16))) uint16_t xs[NS][2][BM * XP];
+  __shared__ __attribute__((aligned(16))) uint16_t xl[NS][2][kSplitX ? BM * XP : 8];
+  // after the K loop the slices' partial results go to the X stages when they
+  // fit there, else to an array of their own
+  constexpr int kRed = NS > 1 ? NS * kThreads * 4 * MT * NT : 0;
+  constexpr bool kRedInX = kRed * 4 <= (int)sizeof(xs);
+  __shared__ float red_own[kRedInX || kRed == 0 ? 1 : kRed];
+  float* const red = kRedInX ? reinterpret_cast<float*>(&xs[0][0][0]) : red_own;
+  // SZL: the scales (and zero points) of this workgroup's BN columns, all
+  // groups, staged once (they are one contiguous run of each [N, K/G] array);
+  // otherwise each K-block's pair rides in the code ring.
+  __shared__ uint16_t s_lds[SZL ? kSZLds : 1], z_lds[SZL && ASYM ? kSZLds : 1];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave-uniform indices live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3), lane = threadIdx.x & 63;
+  const int slice = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8), stid = threadIdx.x & (kThreads - 1);
   const int lr = lane & 15, lg = lane >> 4;
   const int m0 = blockIdx.y * BM;
   const int nw = blockIdx.x * BN + wave * 16 * NT;
   const int gpr = K / G;
+  const int nblk = K / KB;
+  // this slice's K-blocks (slice boundaries fall on group boundaries)
+  const int gstep = G / KB > 1 ? G / KB : 1;
+  const int bps = ((nblk + NS - 1) / NS + gstep - 1) / gstep * gstep;
+  const int first = slice * bps;
+  const int count = nblk - first < bps ? (nblk - first > 0 ? nblk - first : 0) : bps;
+  const int lastb = count > 0 ? first + count - 1 : nblk - 1;  // clamp target for loads
   const float zsym = (float)(1 << (BITS - 1));
-
-  float4_t acc[MT][NT], part[MT][NT];
-  float xg[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      acc[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
-      part[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xg[mt][i] = 0.f;
-  }
   const uint32_t ones2 = XT::kMagic2 == F16::kMagic2 ? 0x3C003C00u : 0x3F803F80u;
 
-  for (int kb = 0; kb < K; kb += KB) {
-    // Codes of this K-block for every column tile (issued first: HBM latency).
-    BCodes<BITS, KB> bc[NT];
-    const int kbeg = kb + lg * (KB / 4);
+  // This lane's columns (past N: column N - 1, results never stored), as
+  // pointers to its codes of K-block 0.
+  int col[NT];
+  const uint8_t* cptr[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = nw + 16 * nt + lr;
+    col[nt] = n < N ? n : N - 1;
+    cptr[nt] = packed + (int64_t)col[nt] * (K / 8 * BITS) +
+               (BITS == 4 ? lg * (KB / 8) : (lg * (KB / 4) / 32) * 12);
+  }
+  auto load_block = [&](BBlock<BITS, KB> (&b)[NT], int blk) {
+    const int kb = blk * KB;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      // columns past N load row N-1 (always valid); their results are never stored
-      const int n = nw + 16 * nt + lr;
-      load_b<BITS, KB>(packed, n < N ? n : N - 1, K, kbeg, bc[nt]);
+      const uint8_t* p = cptr[nt] + (BITS == 4 ? kb / 2 : (kb / 32) * 12);
+      if constexpr (BITS == 4) {
+        if constexpr (KB == 128) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) b[nt].c.w[j] = v[j];
+        } else if constexpr (KB == 64) {
+          const uint2 v = *reinterpret_cast<const uint2*>(p);
+          b[nt].c.w[0] = v.x;
+          b[nt].c.w[1] = v.y;
+        } else {
+          b[nt].c.w[0] = *reinterpret_cast<const uint32_t*>(p);
+        }
+      } else {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+        b[nt].c.w[0] = q[0];
+        b[nt].c.w[1] = q[1];
+        b[nt].c.w[2] = q[2];
+      }
+      if constexpr (!SZL) {
+        const int64_t gi = (int64_t)col[nt] * gpr + kb / G;
+        b[nt].s16 = scales[gi];
+        b[nt].z16 = ASYM ? zeros[gi] : (uint16_t)0;
+      }
     }
+  };
+  if constexpr (SZL) {
+    const int n_base = blockIdx.x * BN;
+    const int cnt = BN * gpr;
+    for (int i = threadIdx.x; i < cnt; i += kThreads * NS) {
+      const int c = i / gpr;
+      const int64_t gi = (int64_t)(n_base + c < N ? n_base + c : N - 1) * gpr + (i - c * gpr);
+      s_lds[i] = scales[gi];
+      if (ASYM) z_lds[i] = zeros[gi];
+    }
+  }
 
-    __syncthreads();  // previous block's LDS readers are done
-    for (int it = threadIdx.x; it < BM * SEG; it += kThreads) {
+  // X staging: thread t owns segments t + 256 u (row it / SEG, segment it %
+  // SEG); rows past M read row M - 1 (their outputs are never stored).
+  struct XRegs {
+    u32x4_t v[XU];
+  };
+  const uint16_t* xptr[XU];
+#pragma unroll
+  for (int u = 0; u < XU; ++u) {
+    const int it = stid + kThreads * u;
+    const int m = (it < UNITS ? it : UNITS - 1) / SEG, seg = it % SEG;
+    const int row = m0 + m < M ? m0 + m : M - 1;
+    xptr[u] = X + (int64_t)row * K + 8 * seg;
+  }
+  auto load_x = [&](XRegs& xr, int blk) {
+#pragma unroll
+    for (int u = 0; u < XU; ++u) xr.v[u] = *reinterpret_cast<const u32x4_t*>(xptr[u] + blk * KB);
+  };
+  auto store_x = [&](const XRegs& xr, int st, int blk) {
+    const int kb = blk * KB;
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int it = stid + kThreads * u;
+      if (UNITS % kThreads != 0 && it >= UNITS) break;
       const int m = it / SEG, seg = it - m * SEG;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u}, vl = v;
-      if (m0 + m < M) v = *reinterpret_cast<const u32x4_t*>(X + (int64_t)(m0 + m) * K + kb + 8 * seg);
+      u32x4_t v = xr.v[u], vl = u32x4_t{0u, 0u, 0u, 0u};
       if (SCALE) {
         const float4_t s0 = *reinterpret_cast<const float4_t*>(s + kb + 8 * seg);
         const float4_t s1 = *reinterpret_cast<const float4_t*>(s + kb + 8 * seg + 4);
@@ -152,54 +243,64 @@ __global__ __launch_bounds__(kThreads) void gemm_direct_kernel(
             vl[e] = (uint32_t)XT::from_f32(a0 - XT::to_f32(h0)) | ((uint32_t)XT::from_f32(a1 - XT::to_f32(h1)) << 16);
         }
       }
-      *reinterpret_cast<u32x4_t*>(&xs[m * XP + 8 * seg]) = v;
-      if (kSplitX) *reinterpret_cast<u32x4_t*>(&xl[m * XP + 8 * seg]) = vl;
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ps = XT::dot2(v[e], ones2, ps);
-      if (kSplitX) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ps = XT::dot2(vl[e], ones2, ps);
-      }
-      ps = team_sum(ps, SEG);
-      if (seg == 0) xsum_s[m] = ps;
+      *reinterpret_cast<u32x4_t*>(&xs[slice][st][m * XP + 8 * seg]) = v;
+      if (kSplitX) *reinterpret_cast<u32x4_t*>(&xl[slice][st][m * XP + 8 * seg]) = vl;
     }
-    __syncthreads();
+  };
 
-    const int t0 = BITS == 3 ? ((kbeg & 31) >> 1) : 0;
+  // part: sum over the group of x (MAGIC + u); xg: sum of x over the group,
+  // from an MFMA against an all-ones B fragment (same C layout as part).
+  float4_t acc[MT][NT], part[MT][NT], xg[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      acc[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+      part[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    xg[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const u32x4_t ones_frag = u32x4_t{ones2, ones2, ones2, ones2};
+
+  const int t0 = BITS == 3 ? (((lg * (KB / 4)) & 31) >> 1) : 0;
+  const uint32_t magic2 = vgpr_const(XT::kMagic2);
+  int szrow[NT];  // this lane's row in the staged scales / zeros
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) szrow[nt] = (wave * 16 * NT + 16 * nt + lr) * gpr;
+  auto compute = [&](const BBlock<BITS, KB> (&b)[NT], int st, int blk) {
 #pragma unroll
     for (int q = 0; q < KB / 32; ++q) {
       u32x4_t a[MT], al[kSplitX ? MT : 1];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        a[mt] = *reinterpret_cast<const u32x4_t*>(&xs[(16 * mt + lr) * XP + lg * (KB / 4) + 8 * q]);
-        if constexpr (kSplitX)
-          al[mt] = *reinterpret_cast<const u32x4_t*>(&xl[(16 * mt + lr) * XP + lg * (KB / 4) + 8 * q]);
+        a[mt] = *reinterpret_cast<const u32x4_t*>(&xs[slice][st][(16 * mt + lr) * XP + lg * (KB / 4) + 8 * q]);
+        xg[mt] = XT::mfma16x16x32(a[mt], ones_frag, xg[mt]);
+        if constexpr (kSplitX) {
+          al[mt] = *reinterpret_cast<const u32x4_t*>(&xl[slice][st][(16 * mt + lr) * XP + lg * (KB / 4) + 8 * q]);
+          xg[mt] = XT::mfma16x16x32(al[mt], ones_frag, xg[mt]);
+        }
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const u32x4_t b = b_fragment<BITS, KB, XT>(bc[nt], q, t0);
+        const u32x4_t bf = b_fragment<BITS, KB, XT>(b[nt].c, q, t0, magic2);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          part[mt][nt] = XT::mfma16x16x32(a[mt], b, part[mt][nt]);
-          if constexpr (kSplitX) part[mt][nt] = XT::mfma16x16x32(al[mt], b, part[mt][nt]);
+          part[mt][nt] = XT::mfma16x16x32(a[mt], bf, part[mt][nt]);
+          if constexpr (kSplitX) part[mt][nt] = XT::mfma16x16x32(al[mt], bf, part[mt][nt]);
         }
       }
     }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xg[mt][i] += xsum_s[16 * mt + 4 * lg + i];
-
-    if ((kb + KB) % G == 0) {
-      const int g = kb / G;
+    if (((blk + 1) * KB) % G == 0) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int n = nw + 16 * nt + lr;
-        float S = 0.f, Z = zsym;
-        if (n < N) {
-          S = half_bits_to_f32(scales[(int64_t)n * gpr + g]);
-          if (ASYM) Z = half_bits_to_f32(zeros[(int64_t)n * gpr + g]);
+        float S, Z = zsym;
+        if constexpr (SZL) {
+          const int li = szrow[nt] + (blk * KB) / G;
+          S = half_bits_to_f32(s_lds[li]);
+          if (ASYM) Z = half_bits_to_f32(z_lds[li]);
+        } else {
+          S = half_bits_to_f32(b[nt].s16);
+          if (ASYM) Z = half_bits_to_f32(b[nt].z16);
         }
         const float c = XT::kMagic + Z;
 #pragma unroll
@@ -210,9 +311,77 @@ __global__ __launch_bounds__(kThreads) void gemm_direct_kernel(
         }
       }
 #pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xg[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  // Two rings of P blocks: ring A holds the codes of the slice's blocks
+  // s P .. s P + P - 1 (and the X of the block after each), ring B those of
+  // the next P blocks.  A loop iteration runs super-blocks s (ring A) and
+  // s + 1 (ring B); ring B is refilled after the first step of A, ring A after
+  // the first step of B, so every load has about P steps to arrive, and the
+  // only registers read across the loop back edge (ring A at the top) were
+  // loaded a whole super-block earlier.  Block indices past the slice's end
+  // are clamped (reloads whose results are never used), which keeps every
+  // load in bounds.  Every wave runs the same bps steps (one barrier each).
+  auto clampb = [&](int lb) { return first + lb < lastb ? first + lb : lastb; };
+  BBlock<BITS, KB> ra[P][NT], rb[P][NT];
+  XRegs xa[P], xb[P];
+  auto fill = [&](BBlock<BITS, KB> (&r)[P][NT], XRegs (&x)[P], int lb0) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      load_block(r[j], clampb(lb0 + j));
+      load_x(x[j], clampb(lb0 + j + 1));
+    }
+  };
+  auto run = [&](const BBlock<BITS, KB> (&r)[NT], const XRegs& x, int lb) {
+    if (lb < bps) {  // uniform across the workgroup
+      if (lb < count) {  // uniform across the slice
+        const int st = lb & 1;
+        compute(r, st, first + lb);
+        store_x(x, st ^ 1, clampb(lb + 1));
+      }
+      __syncthreads();
+    }
+  };
+  {
+    XRegs x0;
+    load_x(x0, clampb(0));
+    fill(ra, xa, 0);
+    store_x(x0, 0, clampb(0));
+  }
+  __syncthreads();
+  for (int base = 0; base < bps; base += 2 * P) {
+    run(ra[0], xa[0], base);
+    fill(rb, xb, base + P);
+#pragma unroll
+    for (int j = 1; j < P; ++j) run(ra[j], xa[j], base + j);
+    run(rb[0], xb[0], base + P);
+    fill(ra, xa, base + 2 * P);
+#pragma unroll
+    for (int j = 1; j < P; ++j) run(rb[j], xb[j], base + P + j);
+  }
+
+  if constexpr (NS > 1) {
+    // sum the slices' partial results (slice 0 keeps the total)
+    float* my = red + (slice * kThreads + stid) * 4 * MT * NT;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) my[(mt * NT + nt) * 4 + i] = acc[mt][nt][i];
+    __syncthreads();
+    if (slice != 0) return;
+#pragma unroll
+    for (int q = 1; q < NS; ++q) {
+      const float* other = red + (q * kThreads + stid) * 4 * MT * NT;
+#pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xg[mt][i] = 0.f;
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][nt][i] += other[(mt * NT + nt) * 4 + i];
     }
   }
 
@@ -230,22 +399,39 @@ __global__ __launch_bounds__(kThreads) void gemm_direct_kernel(
   }
 }
 
+// K-blocks per register ring (two rings: codes and X are loaded up to two
+// rings ahead); 2 measured best of 2 / 4 / 6.
+constexpr int kDirectRing = 2;
+// K slices per workgroup (4 waves each): two (one when X is staged twice, as
+// the bf16 pair hi + lo of x / s), so that two workgroups share a CU; four
+// slices leave one workgroup per CU and measure slower.
+template <int MT, int NT, bool SCALE, bool SPLITX>
+constexpr int kDirectSlices() {
+  return NT > 1 || SPLITX ? 1 : 2;
+}
+
+template <int BITS, bool ASYM, class XT, int MT, int NT, int KB, bool SZL, bool SCALE>
+hipError_t launch_sz(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
+                     int64_t M, int64_t N, int64_t K, int G, void* Y, hipStream_t stream) {
+  constexpr bool kSplitX = SCALE && XT::kMagic2 == BF16::kMagic2;
+  constexpr int NS = kDirectSlices<MT, NT, SCALE, kSplitX>();
+  const dim3 grid((unsigned)((N + 64 * NT - 1) / (64 * NT)), (unsigned)((M + 16 * MT - 1) / (16 * MT)));
+  hipLaunchKernelGGL((gemm_direct_kernel<BITS, ASYM, XT, MT, NT, KB, SCALE, kDirectRing, SZL, NS>), grid,
+                     dim3(kThreads * NS), 0, stream, static_cast<const uint16_t*>(X), s,
+                     static_cast<const uint8_t*>(packed), static_cast<const uint16_t*>(scales),
+                     static_cast<const uint16_t*>(zeros), (int)M, (int)N, (int)K, G, static_cast<uint16_t*>(Y));
+  return hipGetLastError();
+}
+
 template <int BITS, bool ASYM, class XT, int MT, int NT, int KB>
 hipError_t launch_tile(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
                        int64_t M, int64_t N, int64_t K, int G, void* Y, hipStream_t stream) {
-  const dim3 grid((unsigned)((N + 64 * NT - 1) / (64 * NT)), (unsigned)((M + 16 * MT - 1) / (16 * MT)));
-  if (s) {
-    hipLaunchKernelGGL((gemm_direct_kernel<BITS, ASYM, XT, MT, NT, KB, true>), grid, dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
-                       static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N,
-                       (int)K, G, static_cast<uint16_t*>(Y));
-  } else {
-    hipLaunchKernelGGL((gemm_direct_kernel<BITS, ASYM, XT, MT, NT, KB, false>), grid, dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
-                       static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N,
-                       (int)K, G, static_cast<uint16_t*>(Y));
-  }
-  return hipGetLastError();
+  const bool szl = 64 * NT * (K / G) <= kSZLds;
+  if (s)
+    return szl ? launch_sz<BITS, ASYM, XT, MT, NT, KB, true, true>(X, s, packed, scales, zeros, M, N, K, G, Y, stream)
+               : launch_sz<BITS, ASYM, XT, MT, NT, KB, false, true>(X, s, packed, scales, zeros, M, N, K, G, Y, stream);
+  return szl ? launch_sz<BITS, ASYM, XT, MT, NT, KB, true, false>(X, s, packed, scales, zeros, M, N, K, G, Y, stream)
+             : launch_sz<BITS, ASYM, XT, MT, NT, KB, false, false>(X, s, packed, scales, zeros, M, N, K, G, Y, stream);
 }
 
 template <int BITS, bool ASYM, class XT, int KB>

@@ -69,14 +69,6 @@ __device__ inline void load_codes(const uint8_t* __restrict__ p, Codes<BITS>& c)
   }
 }
 
-// A constant the compiler cannot fold: keeps MAGIC in a VGPR so that
-// (w & mask) | MAGIC becomes one v_and_or_b32 with the mask in an SGPR.
-__device__ inline uint32_t vgpr_const(uint32_t v) {
-  uint32_t r;
-  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
-  return r;
-}
-
 // Activation sums of one chunk: part[0] over the pairs t = 0, 2 of every
 // 8-weight word, part[1] over t = 1, 3.
 struct XSums {

@@ -67,6 +67,14 @@ struct BF16 {
 
 // 4-bit word holding k in [8j, 8j+8): pair t (k = 8j+2t, 8j+2t+1) at bits
 // [4t, 4t+4) and [16+4t, 16+4t+4).
+// A constant the compiler cannot fold: keeps MAGIC in a VGPR so that
+// (w & mask) | MAGIC becomes one v_and_or_b32 with the mask in an SGPR.
+__device__ inline uint32_t vgpr_const(uint32_t v) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
 __device__ inline uint32_t pair4(uint32_t w, int t, uint32_t magic2) {
   return ((w >> (4 * t)) & 0x000F000Fu) | magic2;
 }

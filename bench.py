@@ -237,6 +237,45 @@ def time_rows(torch, ops, synth):
         del sets, W
     rows["c3_decode_gemv_awq"] = c3
 
+    # Fused projections: q/k/v (N = 3 x 4096) and gate/up (N = 2 x 11008) share
+    # the input and its AWQ scale, so one launch over the stacked rows serves
+    # them; compared with the sum of the separate launches above.
+    fused = {}
+    for name, idx in (("qkv", [0, 1, 2]), ("gate_up", [4, 5])):
+        lins = [synth.c3_linear(i) for i in idx]
+        K = lins[0].K
+        s = torch.from_numpy(lins[0].act_scale).to(dev)
+        x = torch.from_numpy(lins[0].X[0]).to(dev)
+        Ws = [torch.from_numpy(l.W).to(dev) for l in lins]
+        N = sum(l.N for l in lins)
+        nb = gemv_bytes(N, K, 4, 128, True, act_scale=True)
+        R = rotate_count(nb)
+        sets = [ops.quantize_pack_fused(Ws, 4, 128, True, s) for _ in range(R)]
+        us = burst_us(torch, [lambda j=j: ops.gemv_fused(x, *sets[j % R], K, 4, 128, s) for j in range(10 * R)])
+        sep = sum(c3[l.name]["us"] for l in lins)
+        fused[name] = {"N": N, "K": K, "us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
+                       "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": nb,
+                       "separate_us_sum": round(sep, 3), "speedup_vs_separate": round(sep / us, 3)}
+        del sets, Ws
+    rows["fused_projection_gemv_awq"] = fused
+
+    # Group sizes 32 / 64 / K on the decode shape (M=1, K=N=8192, 4-bit asym).
+    lin = synth.c2_decode()
+    W = torch.from_numpy(lin.W).to(dev)
+    x = torch.from_numpy(lin.X[0]).to(dev)
+    gs = {}
+    for G in (32, 64, 128, lin.K):
+        nb = gemv_bytes(lin.N, lin.K, 4, G, True)
+        R = rotate_count(nb)
+        sets = [ops.quantize_pack(W, 4, G, True) for _ in range(R)]
+        y = torch.empty(lin.N, dtype=torch.float16, device=dev)
+        us = burst_us(torch, [lambda j=j: ops.gemv(x, *sets[j % R], lin.N, lin.K, 4, G, out=y) for j in range(10 * R)])
+        gs[f"G{G}"] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
+                       "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": nb}
+        del sets
+    del W
+    rows["group_size_gemv_c2"] = gs
+
     # Small-batch GEMM, M = 4 / 16 / 64, K = 8192, N = 28672.
     c4 = {}
     W, W_np = None, None

@@ -217,6 +217,37 @@ def test_gemv_llama_linears_with_awq_bf16(i):
     gemv_case(synth.c3_linear(i), 4, True, "bf16")
 
 
+# Fused projections: q/k/v (and gate/up) read the same input and AWQ scale,
+# so one packed set over the stacked rows serves all of them in one launch.
+@pytest.mark.parametrize("which,bits,asym", [("qkv", 4, True), ("gate_up", 4, True), ("qkv", 3, False)])
+def test_fused_projection_gemv(which, bits, asym):
+    idx = [0, 1, 2] if which == "qkv" else [4, 5]
+    lins = [synth.c3_linear(i) for i in idx]
+    K = lins[0].K
+    x, s = lins[0].X[0], lins[0].act_scale  # the shared input and its scale
+    Ws = [gpu_f16(l.W) for l in lins]
+    packed, scales, zeros, sizes = ops.quantize_pack_fused(Ws, bits, 128, asym, gpu_f32(s))
+    sep = [ops.quantize_pack(W, bits, 128, asym, gpu_f32(s)) for W in Ws]
+    torch.cuda.synchronize()
+    assert sizes == [l.N for l in lins]
+    assert np.array_equal(packed.cpu().numpy(), np.concatenate([p[0].cpu().numpy() for p in sep]))
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16),
+                          np.concatenate([p[1].cpu().numpy() for p in sep]).view(np.uint16))
+    if asym:
+        assert np.array_equal(zeros.cpu().numpy().view(np.uint16),
+                              np.concatenate([p[2].cpu().numpy() for p in sep]).view(np.uint16))
+    ys = ops.gemv_fused(gpu_f16(x), packed, scales, zeros, sizes, K, bits, 128, gpu_f32(s))
+    for y, p, l in zip(ys, sep, lins):
+        y_sep = ops.gemv(gpu_f16(x), *p, l.N, K, bits, 128, gpu_f32(s))
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), y_sep.cpu().numpy().view(np.uint16))
+    W_all = np.concatenate([l.W for l in lins])
+    _, _, _, q = O.quantize_pack(W_all, bits, 128, asym, s)
+    y_ref = O.gemm(O.activations_f64(x[None, :], "f16"), O.dequantize(q), s)[0]
+    err = O.rel_l2(np.concatenate([y.cpu().numpy() for y in ys]).astype(np.float64), y_ref)
+    _say(f"fused {which} N={sum(sizes)} K={K} bits={bits} asym={asym}: rel_l2={err:.2e}")
+    assert err <= REL_L2
+
+
 @pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (67, 160), (129, 640), (33, 2048 + 128), (250, 8192 + 512),
                                  (17, 16384), (5, 20480)])
 def test_gemv_ragged_shapes(N, K):

@@ -38,9 +38,22 @@ namespace woq {
 namespace {
 
 constexpr int kMaxSegments = 8;      // K <= 8 * 64 * 32 = 16384 on this path
-constexpr int kTargetWaves = 8;      // waves per workgroup
-constexpr int kTargetBlocks = 1024;  // workgroups sweeping the matrix together
-constexpr int kPrefetch = 2;         // steps of code loads in flight ahead of compute
+#ifndef WOQ_GEMV_WAVES
+#define WOQ_GEMV_WAVES 8
+#endif
+constexpr int kTargetWaves = WOQ_GEMV_WAVES;  // waves per workgroup
+#ifndef WOQ_GEMV_BLOCKS
+#define WOQ_GEMV_BLOCKS 1024
+#endif
+#ifndef WOQ_GEMV_MAXSTEPS
+#define WOQ_GEMV_MAXSTEPS 4
+#endif
+#ifndef WOQ_GEMV_PREFETCH
+#define WOQ_GEMV_PREFETCH 2
+#endif
+constexpr int kTargetBlocks = WOQ_GEMV_BLOCKS;   // workgroups sweeping the matrix together
+constexpr int kMaxSteps = WOQ_GEMV_MAXSTEPS;     // row steps per workgroup (at most)
+constexpr int kPrefetch = WOQ_GEMV_PREFETCH;     // steps of code loads in flight ahead of compute
 
 struct __attribute__((packed, aligned(4))) U32x3 {
   uint32_t a, b, c;
@@ -139,7 +152,7 @@ struct StepLoads {
 // partials [STEPS][waves][64] floats.
 //
 // SPR_T > 0 fixes the shape at compile time: K = 2048 * SPR_T (every segment
-// full), group size 128, RPB = max(1, 8 / SPR_T) rows per workgroup.  SPR_T == 0
+// full), group size 128, RPB = max(1, kTargetWaves / SPR_T) rows per workgroup.  SPR_T == 0
 // is the general path (any K <= 16384 that is a multiple of 32, any group
 // size that is a multiple of 32), with the shape passed at run time.
 template <int BITS, bool ASYM, class XT, bool SCALE, int STEPS, int SPR_T, int PASSES>
@@ -157,7 +170,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
   const int K = kFixed ? 2048 * SPR_T : K_rt;
   const int G = kFixed ? 128 : G_rt;
   const int spr = kFixed ? SPR_T : spr_rt;
-  const int rpb = kFixed ? (SPR_T >= 8 ? 1 : 8 / SPR_T) : rpb_rt;
+  const int rpb = kFixed ? (SPR_T >= kTargetWaves ? 1 : kTargetWaves / SPR_T) : rpb_rt;
   const int nthreads = kFixed ? rpb * spr * 64 : (int)blockDim.x;
   const int cpr = K >> 5;  // chunks per row
   uint32_t* xsh = lds;
@@ -317,15 +330,25 @@ hipError_t launch_scale(const void* x, const float* s, const void* packed, const
   const int rpb = spr >= kTargetWaves ? 1 : kTargetWaves / spr;
   const int64_t groups = (N + rpb - 1) / rpb;
   int steps = 1;
-  while (steps < 4 && groups / (2 * steps) >= kTargetBlocks) steps *= 2;
+  while (steps < kMaxSteps && groups / (2 * steps) >= kTargetBlocks) steps *= 2;
   const int64_t blocks = (groups + steps - 1) / steps;
   switch (steps) {
     case 1:
       return launch_steps<BITS, ASYM, XT, SCALE, 1>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, y, stream);
     case 2:
       return launch_steps<BITS, ASYM, XT, SCALE, 2>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, y, stream);
-    default:
+    case 4:
       return launch_steps<BITS, ASYM, XT, SCALE, 4>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, y, stream);
+#if WOQ_GEMV_MAXSTEPS >= 8
+    case 8:
+      return launch_steps<BITS, ASYM, XT, SCALE, 8>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, y, stream);
+#endif
+#if WOQ_GEMV_MAXSTEPS >= 16
+    case 16:
+      return launch_steps<BITS, ASYM, XT, SCALE, 16>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, y, stream);
+#endif
+    default:
+      return hipErrorInvalidValue;
   }
 }
 

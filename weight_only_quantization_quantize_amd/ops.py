@@ -6,7 +6,7 @@ library.  Nothing is computed here.
 """
 from __future__ import annotations
 
-from typing import Optional, Tuple
+from typing import Optional, Sequence, Tuple
 
 import torch
 
@@ -134,3 +134,51 @@ def dequantize(
                    int(zeros is not None), out.data_ptr(), _stream(packed))
     _lib.check(st, "woq_dequantize")
     return out
+
+
+def quantize_pack_fused(
+    Ws: Sequence[torch.Tensor],
+    bits: int = 4,
+    group_size: int = 128,
+    asymmetric: bool = True,
+    act_scale: Optional[torch.Tensor] = None,
+):
+    """Quantize several weight matrices that read the same input (q/k/v, or
+    gate/up) into one packed set whose rows are theirs, stacked: matrix i
+    fills rows [sum(N_<i), sum(N_<=i)) of each output, written in place by one
+    woq_quantize_pack call per matrix.  A single gemv/gemm over N = sum(N_i)
+    then serves all of them.  Returns (packed, scales, zeros | None, sizes)."""
+    if not Ws:
+        raise ValueError("need at least one matrix")
+    K = Ws[0].shape[1]
+    if any(W.dim() != 2 or W.shape[1] != K for W in Ws):
+        raise ValueError("all matrices must be [N_i, K] with the same K")
+    sizes = [int(W.shape[0]) for W in Ws]
+    N = sum(sizes)
+    dev = Ws[0].device
+    packed = torch.empty((N, packed_bytes(1, K, bits)), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // group_size), dtype=torch.float16, device=dev)
+    zeros = torch.empty_like(scales) if asymmetric else None
+    row = 0
+    for W, n in zip(Ws, sizes):
+        quantize_pack(W, bits, group_size, asymmetric, act_scale,
+                      out=(packed[row:row + n], scales[row:row + n], None if zeros is None else zeros[row:row + n]))
+        row += n
+    return packed, scales, zeros, sizes
+
+
+def gemv_fused(
+    x: torch.Tensor,
+    packed: torch.Tensor,
+    scales: torch.Tensor,
+    zeros: Optional[torch.Tensor],
+    sizes: Sequence[int],
+    K: int,
+    bits: int = 4,
+    group_size: int = 128,
+    act_scale: Optional[torch.Tensor] = None,
+) -> Tuple[torch.Tensor, ...]:
+    """One GEMV launch over a set made by quantize_pack_fused; returns the
+    outputs of the individual matrices as views of one [sum(N_i)] vector."""
+    y = gemv(x, packed, scales, zeros, sum(sizes), K, bits, group_size, act_scale)
+    return tuple(y.split(list(sizes)))

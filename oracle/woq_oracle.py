@@ -50,6 +50,9 @@ reason, in the design notes of the repository):
 * The AWQ fold multiplies W[n,k] by s[k] in binary32 before the group
   statistics; the GEMV/GEMM divides x by s (exactly, in fp64, here).
 * Dequantization and products are exact / fp64: w_hat = (u - Z) * S.
+* AWQ search: alpha on the grid i / n (n = 20), s = max(mean|x|, 1e-4)^alpha
+  with no further normalization, error = ||X W^T - (X/s) Q(W s)^T||_F^2 over
+  the calibration tokens, first minimum wins.
 
 Parity pins for every function here live in ``tests/test_oracle.py``.
 """
@@ -73,6 +76,11 @@ __all__ = [
     "gemm",
     "quantize_pack",
     "rel_l2",
+    "awq_alphas",
+    "awq_channel_mean",
+    "awq_scale_for",
+    "awq_loss",
+    "awq_search",
 ]
 
 
@@ -303,3 +311,58 @@ def rel_l2(y: np.ndarray, y_ref: np.ndarray) -> float:
     den = np.linalg.norm(y_ref.ravel())
     num = np.linalg.norm((y - y_ref).ravel())
     return float(num / den) if den > 0 else float(num)
+
+
+# --------------------------------------------------------------------------
+# AWQ scale search
+# --------------------------------------------------------------------------
+
+AWQ_SCALE_FLOOR = 1e-4  # reading: per-channel scales are kept at or above this
+
+
+def awq_alphas(n_grid: int) -> np.ndarray:
+    """The exponents tried: alpha_i = i / n_grid, i = 0 .. n_grid - 1."""
+    return np.arange(n_grid, dtype=np.float64) / n_grid
+
+
+def awq_channel_mean(X64: np.ndarray) -> np.ndarray:
+    """Mean absolute activation of each input channel over the calibration
+    tokens: the statistic Lab 4's forward hooks record ("MIT 6.5940 Lab 4 +
+    Lab 5", Lab 4 "Starting point and setup")."""
+    return np.abs(np.asarray(X64, dtype=np.float64)).mean(axis=0)
+
+
+def awq_scale_for(mean_abs: np.ndarray, alpha: float) -> np.ndarray:
+    """s = max(mean|x|, floor)^alpha, in fp32.  alpha = 0 gives s = 1 (plain
+    RTN); larger alpha scales the channels that see large activations up."""
+    m = np.maximum(np.asarray(mean_abs, dtype=np.float64), AWQ_SCALE_FLOOR)
+    return np.power(m, alpha).astype(np.float32)
+
+
+def awq_loss(X64: np.ndarray, W: np.ndarray, s: np.ndarray, bits: int, group_size: int,
+             asymmetric: bool) -> float:
+    """Output reconstruction error of one layer for one scale vector:
+    || X W^T - (X / s) Q(W s)^T ||_F^2 in fp64, the layer-wise objective of
+    "Quantising Large Language Models ...", section "Post-training methods
+    for 4-bit weights", with the scale applied as in Lab 4 Question 2 (scale
+    the weight channel up, quantize, divide the activation)."""
+    X64 = np.asarray(X64, dtype=np.float64)
+    y_ref = X64 @ np.asarray(W, dtype=np.float32).astype(np.float64).T
+    q = quantize(W, bits, group_size, asymmetric, s)
+    y_q = gemm(X64, dequantize(q), s)
+    return float(np.sum((y_ref - y_q) ** 2))
+
+
+def awq_search(X64: np.ndarray, W: np.ndarray, bits: int, group_size: int, asymmetric: bool,
+               n_grid: int = 20):
+    """Grid search of the AWQ exponent: for each alpha, compute the scale,
+    scale the weights up, quantize, scale the activations down and measure
+    the output error; the first alpha with the smallest error wins ("MIT
+    6.5940 Lab 4 + Lab 5", Question 2, the search loop).
+
+    Returns (losses fp64 [n_grid], best index, best scale fp32 [K])."""
+    m = awq_channel_mean(X64)
+    losses = np.array([awq_loss(X64, W, awq_scale_for(m, a), bits, group_size, asymmetric)
+                       for a in awq_alphas(n_grid)])
+    best = int(np.argmin(losses))
+    return losses, best, awq_scale_for(m, awq_alphas(n_grid)[best])

@@ -37,6 +37,13 @@ MUTATIONS = {
     "gemm_scale_multiplied": ("X64 = X64 / np.asarray(act_scale", "X64 = X64 * np.asarray(act_scale"),
     "fold_divides": ("return np.multiply(w, s[None, :], dtype=np.float32)",
                      "return np.divide(w, s[None, :], dtype=np.float32)"),
+    "awq_activation_not_divided": ("    y_q = gemm(X64, dequantize(q), s)\n", "    y_q = gemm(X64, dequantize(q), None)\n"),
+    "awq_mean_not_absolute": ("return np.abs(np.asarray(X64, dtype=np.float64)).mean(axis=0)",
+                              "return np.asarray(X64, dtype=np.float64).mean(axis=0)"),
+    "awq_argmax": ("best = int(np.argmin(losses))", "best = int(np.argmax(losses))"),
+    "awq_loss_not_squared": ("return float(np.sum((y_ref - y_q) ** 2))", "return float(np.sum(np.abs(y_ref - y_q)))"),
+    "awq_alpha_grid_inclusive": ("return np.arange(n_grid, dtype=np.float64) / n_grid",
+                                 "return np.arange(n_grid, dtype=np.float64) / (n_grid - 1)"),
     "scale_not_fp16": ("S = np.divide(a, qmax, dtype=np.float32).astype(np.float16)",
                        "S = np.divide(a, qmax, dtype=np.float32).astype(np.float16) * np.float16(1.0009765625)"),
 }

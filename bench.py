@@ -324,6 +324,25 @@ def time_rows(torch, ops, synth):
     del sets, W
     rows["c5_prefill_gemm"] = c5
 
+    # AWQ exponent search (20 exponents) for the q_proj shape on 512
+    # calibration tokens with 1% outlier channels: per exponent one scale,
+    # quantize_pack, prefill-size GEMM and error reduction.
+    lin = synth.c3_linear(0)
+    ch = lin.extra["channels"]
+    Xc = torch.from_numpy(synth.to_f16(synth.activations_f32(synth.CALIBRATION_TOKENS, lin.K, 3200, ch))).to(dev)
+    Wq = torch.from_numpy(lin.W).to(dev)
+    ops.awq_search(Xc, Wq, 4, 128, True, 20)
+    torch.cuda.synchronize()
+    us = burst_us(torch, [lambda: ops.awq_search(Xc, Wq, 4, 128, True, 20)], reps=3)
+    losses, _, best = ops.awq_search(Xc, Wq, 4, 128, True, 20)
+    L = losses.cpu().numpy()
+    b = int(best.cpu().numpy()[0])
+    T, N, K = synth.CALIBRATION_TOKENS, lin.N, lin.K
+    rows["awq_search_q_proj"] = {"T": T, "N": N, "K": K, "n_grid": 20, "ms": round(us / 1e3, 3),
+                                 "gemm_flop": 20 * 2 * T * N * K, "best_alpha": b / 20,
+                                 "loss_best_over_rtn": float(f"{L[b] / L[0]:.4g}")}
+    del Xc, Wq
+
     # quantize_pack over 32 layers of the LLaMA-2-7B linear shapes (weights
     # generated on the device, seed 5100 + layer), 4-bit asym g128.
     shapes = [(N, K) for _, N, K in synth.LLAMA7B_LINEARS]

@@ -151,6 +151,33 @@ woq_status woq_dequantize(const void* packed, const void* scales, const void* ze
                           int64_t N, int64_t K, int32_t bits, int32_t group_size, int32_t asymmetric,
                           float* out, void* stream);
 
+/* AWQ exponent search over one layer ("MIT 6.5940 Lab 4 + Lab 5", Question 2:
+ * compute the scale, scale the weight channels up, quantize, divide the
+ * activations; the layer-wise reconstruction objective of "Quantising Large
+ * Language Models ...", section "Post-training methods for 4-bit weights").
+ *   X          : fp16 [T, K] row-major calibration activations (device)
+ *   W          : fp16 [N, K] row-major weights (device)
+ *   bits, group_size, asymmetric : the quantizer to search for (as above)
+ *   n_grid     : number of exponents, 1 .. 64; alpha_i = i / n_grid
+ *   losses     : out, fp64 [n_grid] (device): || X W^T - (X / s_i) Q(W s_i)^T ||_F^2
+ *                with s_i[k] = fl32(max(mean_t |X[t, k]|, 1e-4)^alpha_i)
+ *   best_scale : out, fp32 [K] (device, 16-byte aligned): s of the first
+ *                alpha with the smallest loss, ready to pass as act_scale
+ *   best_index : out, int32 [1] (device): that alpha's index
+ *   workspace  : device scratch of woq_awq_search_workspace_bytes(...) bytes,
+ *                256-byte aligned, owned by the caller; holds one packed set,
+ *                the reference output X W^T (fp32) and the quantized one.
+ * The loss uses the library's own quantize_pack and GEMM (so the quantized
+ * output is rounded to fp16 as any other call's), an fp32 reference output
+ * and an fp64 sum.  Asynchronous on stream; returns WOQ_ERR_INVALID_ARGUMENT
+ * for bad sizes, pointers or a short workspace. */
+size_t woq_awq_search_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t bits,
+                                      int32_t group_size, int32_t asymmetric);
+woq_status woq_awq_search(const void* X, const void* W, int64_t T, int64_t N, int64_t K,
+                          int32_t bits, int32_t group_size, int32_t asymmetric, int32_t n_grid,
+                          double* losses, float* best_scale, int32_t* best_index,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* woq_status_string(woq_status status);
 

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("woq_quantize_pack", "woq_w4a16_gemv", "woq_w4a16_gemm", "woq_packed_bytes", "woq_workspace_bytes",
-              "woq_status_string", "woq_last_error", "woq_dequantize", "woq_scales_bytes", "woq_layout_version"):
+              "woq_status_string", "woq_last_error", "woq_dequantize", "woq_scales_bytes", "woq_layout_version",
+              "woq_awq_search", "woq_awq_search_workspace_bytes"):
         assert n in names
 
 
@@ -151,6 +152,46 @@ def test_dequantize_rejects(lib):
     assert st == _lib.WOQ_ERR_INVALID_ARGUMENT
     st = lib.woq_dequantize(FAKE, FAKE, FAKE, 64, 256, 4, 128, 1, FAKE + 4, None)
     assert st == _lib.WOQ_ERR_INVALID_ARGUMENT
+
+
+def _awq(lib, **kw):
+    a = dict(X=FAKE, W=FAKE, T=128, N=64, K=256, bits=4, G=128, asym=1, n=20, losses=FAKE, best=FAKE, idx=FAKE,
+             ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.woq_awq_search(a["X"], a["W"], a["T"], a["N"], a["K"], a["bits"], a["G"], a["asym"], a["n"],
+                              a["losses"], a["best"], a["idx"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize(
+    "kw, needle",
+    [
+        (dict(T=0), "T must"),
+        (dict(n=0), "n_grid"),
+        (dict(n=65), "n_grid"),
+        (dict(X=None), "X and W"),
+        (dict(W=FAKE + 8), "X and W must be 16-byte"),
+        (dict(losses=FAKE + 4), "losses"),
+        (dict(best=FAKE + 4), "best_scale"),
+        (dict(idx=None), "best_index"),
+        (dict(ws=FAKE + 128), "workspace must be"),
+        (dict(wsb=1024), "workspace too small"),
+        (dict(bits=2), "bits"),
+    ],
+)
+def test_awq_search_rejects(lib, kw, needle):
+    assert _awq(lib, **kw) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    assert needle in lib.woq_last_error().decode()
+
+
+def test_awq_search_workspace_size(lib):
+    # one packed set, fp16 scales and zeros, fp32 reference and fp16 quantized
+    # outputs, channel means and scales, fp64 partial sums: all 256-byte padded
+    T, N, K = 128, 64, 256
+    need = lib.woq_awq_search_workspace_bytes(T, N, K, 4, 128, 1)
+    parts = [8 * K, 4 * K, N * K // 2, 2 * N * 2, 2 * N * 2, 4 * T * N, 2 * T * N, 8 * 1024]
+    assert need == sum((p + 255) // 256 * 256 for p in parts)
+    assert lib.woq_awq_search_workspace_bytes(0, N, K, 4, 128, 1) == 0
+    assert lib.woq_awq_search_workspace_bytes(T, N, K, 5, 128, 1) == 0
 
 
 def test_oversized_shapes_are_unsupported(lib):

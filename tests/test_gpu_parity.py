@@ -416,3 +416,39 @@ def test_gemm_prefill_full_size_sampled():
     rows = np.sort(np.random.default_rng(5).choice(lin.N, 96, replace=False))
     rows = np.concatenate([rows, [lin.N - 1]])
     gemm_case(lin.W, lin.X, "f16", 4, True, rows=rows, label="c5")
+
+
+# ---------------------------------------------------------------------------
+# AWQ exponent search
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,N,K,bits,asym", [(128, 256, 1024, 4, True), (32, 192, 512, 3, False),
+                                             (256, 320, 2048, 4, False)])
+def test_awq_search_matches_oracle(T, N, K, bits, asym):
+    # Calibration activations with 1% of channels x50 (the LLaMA-shaped
+    # workload's recipe) and N(0, 0.02) weights.
+    seed = T + N + K + bits
+    ch = synth.outlier_channels(K, seed)
+    X = synth.to_f16(synth.activations_f32(T, K, seed + 1, ch))
+    W = synth.weights(N, K, seed + 2)
+    losses, best_scale, best_index = ops.awq_search(gpu_f16(X), gpu_f16(W), bits, 128, asym, 20)
+    torch.cuda.synchronize()
+    L = losses.cpu().numpy()
+    b = int(best_index.cpu().numpy()[0])
+    L_ref, b_ref, s_ref = O.awq_search(X.astype(np.float64), W, bits, 128, asym, 20)
+    # The GPU loss differs from the fp64 one by the fp16 roundings of x * (1/s)
+    # and of the quantized output (about 2^-12 relative each, against a
+    # quantization error of a few percent): 1e-3 relative is ample.
+    rel = np.abs(L / L_ref - 1)
+    _say(f"awq T={T} N={N} K={K} bits={bits} asym={asym}: best {b} (oracle {b_ref}), max rel loss diff {rel.max():.1e}")
+    assert rel.max() < 1e-3
+    srt = np.sort(L_ref)
+    if srt[1] > srt[0] * (1 + 2e-3):  # a clear minimum: the same exponent
+        assert b == b_ref
+    else:  # a near tie: any exponent whose fp64 loss is within the tolerance
+        assert L_ref[b] <= srt[0] * (1 + 2e-3)
+    # the returned scale is the oracle's scale for the chosen exponent
+    s_expect = O.awq_scale_for(O.awq_channel_mean(X.astype(np.float64)), b / 20)
+    assert np.array_equal(best_scale.cpu().numpy(), s_expect)
+    # the search must beat plain RTN on outlier channels
+    assert L[b] < L[0]

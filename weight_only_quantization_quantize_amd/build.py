@@ -18,7 +18,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwoq.so")
 ARCH = os.environ.get("WOQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["woq_api.cpp", "quantize_pack.hip", "gemv.hip", "gemm.hip", "gemm_lds.hip", "dequantize.hip"]
+SOURCES = ["woq_api.cpp", "quantize_pack.hip", "gemv.hip", "gemm.hip", "gemm_lds.hip", "dequantize.hip",
+           "awq_search.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

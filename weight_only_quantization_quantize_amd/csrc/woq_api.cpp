@@ -200,6 +200,39 @@ woq_status woq_dequantize(const void* packed, const void* scales, const void* ze
   WOQ_GUARD_END
 }
 
+size_t woq_awq_search_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t bits, int32_t group_size,
+                                      int32_t asymmetric) {
+  if (T < 1 || check_qparams(N, K, bits, group_size) != WOQ_OK) return 0;
+  return woq::awq_search_workspace_bytes(T, N, K, bits, group_size, asymmetric != 0);
+}
+
+woq_status woq_awq_search(const void* X, const void* W, int64_t T, int64_t N, int64_t K, int32_t bits,
+                          int32_t group_size, int32_t asymmetric, int32_t n_grid, double* losses, float* best_scale,
+                          int32_t* best_index, void* workspace, size_t workspace_bytes, void* stream) {
+  WOQ_GUARD_BEGIN
+  WOQ_TRY(check_qparams(N, K, bits, group_size));
+  if (T < 1) return fail(WOQ_ERR_INVALID_ARGUMENT, "T must be >= 1 (got %lld)", (long long)T);
+  if (T > INT32_MAX / 2 || T * N > (int64_t)1 << 40)
+    return fail(WOQ_ERR_UNSUPPORTED, "T x N too large for this build (T=%lld, N=%lld)", (long long)T, (long long)N);
+  if (n_grid < 1 || n_grid > 64) return fail(WOQ_ERR_INVALID_ARGUMENT, "n_grid must be in [1, 64] (got %d)", n_grid);
+  if (!X || !W) return fail(WOQ_ERR_INVALID_ARGUMENT, "X and W must not be NULL");
+  if (!aligned(X, 16) || !aligned(W, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "X and W must be 16-byte aligned");
+  if (!losses || !aligned(losses, 8)) return fail(WOQ_ERR_INVALID_ARGUMENT, "losses must be non-NULL, 8-byte aligned");
+  if (!best_scale || !aligned(best_scale, 16))
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "best_scale must be non-NULL, 16-byte aligned");
+  if (!best_index || !aligned(best_index, 4))
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "best_index must be non-NULL, 4-byte aligned");
+  const size_t need = woq::awq_search_workspace_bytes(T, N, K, bits, group_size, asymmetric != 0);
+  if (!workspace || !aligned(workspace, 256))
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "workspace too small (%zu bytes, need %zu)", workspace_bytes, need);
+  return from_hip(woq::launch_awq_search(X, W, T, N, K, bits, group_size, asymmetric != 0, n_grid, losses,
+                                         best_scale, best_index, workspace, static_cast<hipStream_t>(stream)),
+                  "awq_search launch");
+  WOQ_GUARD_END
+}
+
 const char* woq_status_string(woq_status status) {
   switch (status) {
     case WOQ_OK:

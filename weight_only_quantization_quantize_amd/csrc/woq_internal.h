@@ -29,6 +29,12 @@ hipError_t launch_gemm_lds(const void* X, int xdtype, const float* act_scale, co
                            const void* scales, const void* zeros, int64_t M, int64_t N, int64_t K, int bits,
                            int group_size, bool asymmetric, void* Y, hipStream_t stream);
 
+// AWQ exponent search (scratch in the caller's workspace).
+size_t awq_search_workspace_bytes(int64_t T, int64_t N, int64_t K, int bits, int group_size, bool asymmetric);
+hipError_t launch_awq_search(const void* X, const void* W, int64_t T, int64_t N, int64_t K, int bits,
+                             int group_size, bool asymmetric, int n_grid, double* losses, float* best_scale,
+                             int32_t* best_index, void* workspace, hipStream_t stream);
+
 // Dequantize to fp32 (test aid).
 hipError_t launch_dequantize(const void* packed, const void* scales, const void* zeros, int64_t N,
                              int64_t K, int bits, int group_size, bool asymmetric, float* out,

@@ -182,3 +182,36 @@ def gemv_fused(
     outputs of the individual matrices as views of one [sum(N_i)] vector."""
     y = gemv(x, packed, scales, zeros, sum(sizes), K, bits, group_size, act_scale)
     return tuple(y.split(list(sizes)))
+
+
+def awq_search(
+    X: torch.Tensor,
+    W: torch.Tensor,
+    bits: int = 4,
+    group_size: int = 128,
+    asymmetric: bool = True,
+    n_grid: int = 20,
+):
+    """AWQ exponent search for one layer on calibration activations X [T, K]
+    (fp16) and weights W [N, K] (fp16).  Returns (losses fp64 [n_grid],
+    best_scale fp32 [K], best_index int32 [1]), all on the device; the
+    workspace is allocated here (PyTorch memory) and released on return."""
+    if X.dtype != torch.float16 or W.dtype != torch.float16 or X.dim() != 2 or W.dim() != 2:
+        raise ValueError("X and W must be 2-D float16 tensors")
+    T, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("X and W must share K")
+    nbytes = int(_lib.call("woq_awq_search_workspace_bytes", T, N, K, bits, group_size, int(asymmetric)))
+    if nbytes == 0:
+        raise ValueError("unsupported shape or quantizer for awq_search")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=X.device)
+    losses = torch.empty(n_grid, dtype=torch.float64, device=X.device)
+    best_scale = torch.empty(K, dtype=torch.float32, device=X.device)
+    best_index = torch.empty(1, dtype=torch.int32, device=X.device)
+    _require_gpu(X, W, ws, losses, best_scale, best_index)
+    st = _lib.call("woq_awq_search", X.data_ptr(), W.data_ptr(), T, N, K, bits, group_size, int(asymmetric), n_grid,
+                   losses.data_ptr(), best_scale.data_ptr(), best_index.data_ptr(), ws.data_ptr(), nbytes,
+                   _stream(X))
+    _lib.check(st, "woq_awq_search")
+    return losses, best_scale, best_index

@@ -53,6 +53,9 @@ reason, in the design notes of the repository):
 * AWQ search: alpha on the grid i / n (n = 20), s = max(mean|x|, 1e-4)^alpha
   with no further normalization, error = ||X W^T - (X/s) Q(W s)^T||_F^2 over
   the calibration tokens, first minimum wins.
+* GPTQ: lambda = 0.01 * mean(diag(2 X^T X)); channels with a zero diagonal get
+  1 and their weights are zeroed; group parameters come from the current
+  (updated) weights when a group's first column is reached.
 
 Parity pins for every function here live in ``tests/test_oracle.py``.
 """
@@ -81,6 +84,10 @@ __all__ = [
     "awq_scale_for",
     "awq_loss",
     "awq_search",
+    "codes_with_params",
+    "gptq_upper_factor",
+    "gptq",
+    "reconstruction_loss",
 ]
 
 
@@ -366,3 +373,95 @@ def awq_search(X64: np.ndarray, W: np.ndarray, bits: int, group_size: int, asymm
                        for a in awq_alphas(n_grid)])
     best = int(np.argmin(losses))
     return losses, best, awq_scale_for(m, awq_alphas(n_grid)[best])
+
+
+# --------------------------------------------------------------------------
+# GPTQ
+# --------------------------------------------------------------------------
+
+GPTQ_DAMP = 0.01  # reading: lambda = 0.01 * mean(diag(2 X^T X))
+
+
+def codes_with_params(w: np.ndarray, S: np.ndarray, Z: Optional[np.ndarray], bits: int,
+                      asymmetric: bool) -> np.ndarray:
+    """Codes of one weight column w [N] (fp32 values) under given per-row
+    group parameters S [N] (fp16) and Z [N] (fp16, asymmetric): the same
+    element rule as ``quantize`` (rne(fl32(w / S)), clipped; S == 0 gives the
+    zero code)."""
+    w = np.asarray(w, dtype=np.float32)
+    S32 = np.asarray(S, dtype=np.float16).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint(np.divide(w, S32, dtype=np.float32))
+    if not asymmetric:
+        half = 2 ** (bits - 1)
+        q = np.where(S32 == 0, np.float32(0), q)
+        return (np.clip(q, -half, half - 1) + half).astype(np.uint8)
+    qu = np.float32(2 ** bits - 1)
+    Zf = np.asarray(Z, dtype=np.float16).astype(np.float32)
+    q = np.where(S32 == 0, -Zf, q)
+    return np.clip(q + Zf, 0, qu).astype(np.uint8)
+
+
+def gptq_upper_factor(X64: np.ndarray, damp: float = GPTQ_DAMP):
+    """U, upper triangular with U^T U = (2 X^T X + lambda I)^-1, i.e. the
+    transposed Cholesky factor of the inverse Hessian ("CMU 11-868 L19-L20",
+    section "The algorithm in four steps", step 1), with lambda = damp *
+    mean(diag(2 X^T X)).  Input channels that never fire (zero diagonal) get a
+    diagonal of 1 and are returned as `dead`."""
+    X64 = np.asarray(X64, dtype=np.float64)
+    K = X64.shape[1]
+    H = 2.0 * (X64.T @ X64)
+    dead = np.diag(H) == 0
+    H[dead, dead] = 1.0
+    H = H + damp * np.mean(np.diag(H)) * np.eye(K)
+    U = np.linalg.cholesky(np.linalg.inv(H)).T
+    return U, dead
+
+
+def gptq(X64: np.ndarray, W: np.ndarray, bits: int, group_size: int, asymmetric: bool,
+         damp: float = GPTQ_DAMP, return_errors: bool = False):
+    """GPTQ in its plain column-by-column form ("CMU 11-868 L19-L20", section
+    "The algorithm in four steps"): for k = 0 .. K-1, quantize column k,
+    divide its rounding error by U[k, k] and subtract err * U[k, j] from every
+    later column j.  (Blocking and lazy batch updates reorder this arithmetic
+    without changing it.)  Group parameters are taken, as the first column of
+    each group is reached, from the group's current (already updated) weights,
+    by the same rules as ``quantize``.  The updates run in fp64; every rounding
+    decision is made on the fp32 value of the current weight.
+
+    Returns a Quantized (and the error matrix E [N, K] with W - w_hat = E U
+    when return_errors)."""
+    W = np.asarray(W)
+    N, K = W.shape
+    assert K % group_size == 0
+    U, dead = gptq_upper_factor(X64, damp)
+    Wf = W.astype(np.float32).astype(np.float64)
+    Wf[:, dead] = 0.0
+    codes = np.zeros((N, K), np.uint8)
+    S = np.zeros((N, K // group_size), np.float16)
+    Z = np.zeros((N, K // group_size), np.float16) if asymmetric else None
+    E = np.zeros((N, K))
+    for k in range(K):
+        g = k // group_size
+        if k % group_size == 0:
+            qg = quantize(Wf[:, k:k + group_size].astype(np.float32), bits, group_size, asymmetric)
+            S[:, g] = qg.scales[:, 0]
+            if asymmetric:
+                Z[:, g] = qg.zeros[:, 0]
+        u = codes_with_params(Wf[:, k].astype(np.float32), S[:, g], None if Z is None else Z[:, g], bits, asymmetric)
+        codes[:, k] = u
+        z = Z[:, g].astype(np.float64) if asymmetric else float(2 ** (bits - 1))
+        w_hat = (u.astype(np.float64) - z) * S[:, g].astype(np.float64)
+        err = (Wf[:, k] - w_hat) / U[k, k]
+        E[:, k] = err
+        Wf[:, k + 1:] -= np.outer(err, U[k, k + 1:])
+    q = Quantized(codes, S, Z, bits, group_size, asymmetric)
+    return (q, E) if return_errors else q
+
+
+def reconstruction_loss(X64: np.ndarray, W: np.ndarray, q: Quantized) -> float:
+    """|| X W^T - X w_hat^T ||_F^2 in fp64: the layer-wise objective GPTQ and
+    RTN are compared on ("CMU 11-868 L19-L20", page 16 / L20 page 5)."""
+    X64 = np.asarray(X64, dtype=np.float64)
+    D = np.asarray(W, dtype=np.float32).astype(np.float64) - dequantize(q)
+    return float(np.sum((X64 @ D.T) ** 2))

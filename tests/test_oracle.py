@@ -494,3 +494,78 @@ def test_awq_search_equal_channel_means_keep_alpha_zero():
     W = (rng.standard_normal((8, 256)) * 0.02).astype(np.float16)
     losses, best, s = O.awq_search(X, W, 4, 128, True, 10)
     assert np.all(losses == losses[0]) and best == 0 and np.all(s == 1)
+
+
+# ---------------------------------------------------------------------------
+# GPTQ ("CMU 11-868 L19-L20", section "The algorithm in four steps")
+# ---------------------------------------------------------------------------
+def _correlated_inputs(seed, T=192, K=256, rank=8):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, rank)) @ rng.standard_normal((rank, K)) + 0.3 * rng.standard_normal((T, K))
+    return X.astype(np.float16).astype(np.float64)
+
+
+def test_gptq_upper_factor_inverts_the_damped_hessian():
+    X = _correlated_inputs(1)
+    U, dead = O.gptq_upper_factor(X)
+    H = 2 * X.T @ X
+    H = H + 0.01 * np.mean(np.diag(H)) * np.eye(H.shape[0])
+    assert not dead.any()
+    assert np.allclose(np.tril(U, -1), 0) and np.all(np.diag(U) > 0)
+    assert np.abs(U.T @ U @ H - np.eye(H.shape[0])).max() < 1e-8
+
+
+@pytest.mark.parametrize("bits,asym,G", [(4, True, 128), (3, False, 32), (4, False, 64)])
+def test_gptq_with_a_diagonal_hessian_is_rtn(bits, asym, G):
+    # Uncorrelated input channels make (2 X^T X + lambda I)^-1 diagonal: no
+    # error is pushed anywhere, and GPTQ must return the RTN codes exactly.
+    rng = np.random.default_rng(bits + G)
+    K, N = 256, 16
+    X = np.diag(rng.uniform(0.5, 3.0, K)).astype(np.float16).astype(np.float64)
+    W = _random_groups(rng, N, K)
+    q = O.gptq(X, W, bits, G, asym)
+    r = O.quantize(W, bits, G, asym)
+    assert np.array_equal(q.codes, r.codes)
+    assert np.array_equal(q.scales.view(np.uint16), r.scales.view(np.uint16))
+    if asym:
+        assert np.array_equal(q.zeros.view(np.uint16), r.zeros.view(np.uint16))
+
+
+def test_gptq_errors_satisfy_w_minus_w_hat_equals_e_u():
+    # Unrolling the column updates: W - w_hat = E U with E the scaled errors.
+    X = _correlated_inputs(2)
+    W = _random_groups(np.random.default_rng(2), 12, 256)
+    q, E = O.gptq(X, W, 4, 128, True, return_errors=True)
+    U, _ = O.gptq_upper_factor(X)
+    D = W.astype(np.float64) - O.dequantize(q)
+    assert np.abs(D - E @ U).max() < 1e-12
+
+
+def test_gptq_beats_rtn_on_correlated_inputs():
+    X = _correlated_inputs(3)
+    W = _random_groups(np.random.default_rng(3), 32, 256)
+    for bits, asym in ((4, True), (3, False)):
+        lg = O.reconstruction_loss(X, W, O.gptq(X, W, bits, 128, asym))
+        lr = O.reconstruction_loss(X, W, O.quantize(W, bits, 128, asym))
+        assert lg < 0.5 * lr
+
+
+def test_gptq_dead_channel_is_zeroed():
+    X = _correlated_inputs(4)
+    X[:, 7] = 0.0
+    W = _random_groups(np.random.default_rng(4), 8, 256)
+    U, dead = O.gptq_upper_factor(X)
+    assert dead[7] and dead.sum() == 1
+    for asym in (True, False):
+        assert np.all(O.dequantize(O.gptq(X, W, 4, 128, asym))[:, 7] == 0)
+
+
+def test_codes_with_params_matches_quantize():
+    rng = np.random.default_rng(5)
+    W = _random_groups(rng, 16, 128)
+    for bits, asym in ((4, True), (3, False), (4, False)):
+        q = O.quantize(W, bits, 128, asym)
+        for k in (0, 5, 127):
+            u = O.codes_with_params(W[:, k].astype(np.float32), q.scales[:, 0], None if q.zeros is None else q.zeros[:, 0],
+                                    bits, asym)
+            assert np.array_equal(u, q.codes[:, k])

@@ -44,6 +44,16 @@ MUTATIONS = {
     "awq_loss_not_squared": ("return float(np.sum((y_ref - y_q) ** 2))", "return float(np.sum(np.abs(y_ref - y_q)))"),
     "awq_alpha_grid_inclusive": ("return np.arange(n_grid, dtype=np.float64) / n_grid",
                                  "return np.arange(n_grid, dtype=np.float64) / (n_grid - 1)"),
+    "gptq_error_not_scaled": ("err = (Wf[:, k] - w_hat) / U[k, k]", "err = (Wf[:, k] - w_hat)"),
+    "gptq_update_sign": ("Wf[:, k + 1:] -= np.outer(err, U[k, k + 1:])", "Wf[:, k + 1:] += np.outer(err, U[k, k + 1:])"),
+    "gptq_update_column_of_factor": ("Wf[:, k + 1:] -= np.outer(err, U[k, k + 1:])",
+                                     "Wf[:, k + 1:] -= np.outer(err, U[k + 1:, k])"),
+    "gptq_factor_not_transposed": ("U = np.linalg.cholesky(np.linalg.inv(H)).T", "U = np.linalg.cholesky(np.linalg.inv(H))"),
+    "gptq_factor_of_hessian": ("U = np.linalg.cholesky(np.linalg.inv(H)).T", "U = np.linalg.cholesky(H).T"),
+    "gptq_hessian_not_doubled": ("H = 2.0 * (X64.T @ X64)", "H = X64.T @ X64"),
+    "gptq_dead_not_zeroed": ("Wf[:, dead] = 0.0", "Wf[:, dead] = Wf[:, dead]"),
+    "gptq_params_from_original_weights": ("qg = quantize(Wf[:, k:k + group_size].astype(np.float32)",
+                                          "qg = quantize(W[:, k:k + group_size].astype(np.float32)"),
     "scale_not_fp16": ("S = np.divide(a, qmax, dtype=np.float32).astype(np.float16)",
                        "S = np.divide(a, qmax, dtype=np.float32).astype(np.float16) * np.float16(1.0009765625)"),
 }

@@ -178,6 +178,40 @@ woq_status woq_awq_search(const void* X, const void* W, int64_t T, int64_t N, in
                           double* losses, float* best_scale, int32_t* best_index,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* GPTQ into layout v1 ("CMU 11-868 L19-L20 Model Quantization", section
+ * "The algorithm in four steps"; the layer-wise objective of "Quantising
+ * Large Language Models ...", section "Post-training methods for 4-bit
+ * weights").
+ *   X          : fp16 [T, K] row-major calibration activations (device)
+ *   W          : fp16 [N, K] row-major weights (device)
+ *   bits, group_size, asymmetric : the quantizer (as above); K % 128 == 0 and
+ *                group_size divides 128 or is a multiple of 128, else
+ *                WOQ_ERR_UNSUPPORTED
+ *   damp       : > 0; lambda = damp * mean(diag H) is added to the diagonal
+ *                of H = 2 X^T X (0.01 is the usual value)
+ *   packed, scales, zeros : out, exactly as woq_quantize_pack writes them
+ *                (zeros only when asymmetric), ready for the GEMV / GEMM with
+ *                act_scale = NULL
+ *   workspace  : device scratch of woq_gptq_workspace_bytes(...) bytes,
+ *                256-byte aligned, owned by the caller (two K x K fp64
+ *                matrices, an fp64 copy of W and 128 fp64 errors per row).
+ * A channel with H[k, k] == 0 (never active in X) gets H[k, k] = 1 and its
+ * weights set to 0 before quantization.  U (upper, U^T U = (H + lambda I)^-1)
+ * comes from a Cholesky factorization and triangular inverse in fp64; columns
+ * are quantized in order, each rounding error divided by U[k, k] and
+ * subtracted, times U[k, j], from every later column j (fp64).  The
+ * parameters of a group come from its current weights when its first column
+ * is reached, and every rounding decision (group statistic, scale, zero
+ * point, code) is made on the fp32 value of the current weight by the rules
+ * above.  Non-finite X or W give unspecified codes.  Asynchronous on stream;
+ * returns WOQ_ERR_INVALID_ARGUMENT for bad sizes, pointers or a short
+ * workspace. */
+size_t woq_gptq_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t bits, int32_t group_size);
+woq_status woq_gptq_quantize_pack(const void* X, const void* W, int64_t T, int64_t N, int64_t K,
+                                  int32_t bits, int32_t group_size, int32_t asymmetric, double damp,
+                                  void* packed, void* scales, void* zeros,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* woq_status_string(woq_status status);
 

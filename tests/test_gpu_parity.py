@@ -452,3 +452,105 @@ def test_awq_search_matches_oracle(T, N, K, bits, asym):
     assert np.array_equal(best_scale.cpu().numpy(), s_expect)
     # the search must beat plain RTN on outlier channels
     assert L[b] < L[0]
+
+
+# ---------------------------------------------------------------------------
+# GPTQ into layout v1
+# ---------------------------------------------------------------------------
+
+def _gptq_gpu(X, W, bits, G, asym):
+    packed, scales, zeros = ops.gptq(gpu_f16(X), gpu_f16(W), bits, G, asym)
+    torch.cuda.synchronize()
+    K = W.shape[1]
+    codes = O.unpack_v1(packed.cpu().numpy(), bits, K)
+    zs = None if zeros is None else zeros.cpu().numpy()
+    return O.Quantized(codes, scales.cpu().numpy(), zs, bits, G, asym), (packed, scales, zeros)
+
+
+def _row_equal(q, r):
+    """Per row: codes, scales and zeros bit-identical."""
+    eq = np.all(q.codes == r.codes, axis=1)
+    eq &= np.all(q.scales.view(np.uint16) == r.scales.view(np.uint16), axis=1)
+    if r.zeros is not None:
+        eq &= np.all(q.zeros.view(np.uint16) == r.zeros.view(np.uint16), axis=1)
+    return eq
+
+
+@pytest.mark.parametrize("bits,asym,G,N,K", [(4, True, 128, 100, 256), (3, False, 32, 70, 384),
+                                              (4, False, 64, 64, 256), (4, True, 256, 65, 256),
+                                              (3, True, 384, 33, 384)])
+def test_gptq_with_a_diagonal_hessian_is_rtn(bits, asym, G, N, K):
+    # One token per channel makes H diagonal, so U is diagonal and no error
+    # moves: GPTQ must return quantize_pack's bytes for W with the dead
+    # channels (never active) zeroed.
+    rng = np.random.default_rng(bits * 1000 + G + N)
+    v = rng.uniform(0.5, 3.0, K)
+    dead = rng.choice(K, 3, replace=False)
+    v[dead] = 0.0
+    X = np.diag(v).astype(np.float16)
+    W = synth.weights_with_outliers(N, K, 11 + N, 12 + N, 13 + N)
+    _say(f"gptq diagonal bits={bits} asym={asym} G={G} N={N} K={K}")
+    q, _ = _gptq_gpu(X, W, bits, G, asym)
+    Wz = W.copy()
+    Wz[:, dead] = 0
+    r = O.quantize(Wz, bits, G, asym)
+    assert np.array_equal(q.codes, r.codes)
+    assert np.array_equal(q.scales.view(np.uint16), r.scales.view(np.uint16))
+    if asym:
+        assert np.array_equal(q.zeros.view(np.uint16), r.zeros.view(np.uint16))
+
+
+@pytest.mark.parametrize("T,N,K,bits,asym,G", [(192, 100, 256, 4, True, 128), (250, 70, 384, 3, False, 32),
+                                               (128, 64, 512, 4, False, 64), (200, 65, 256, 4, True, 256),
+                                               (301, 48, 384, 3, True, 384)])
+def test_gptq_matches_oracle(T, N, K, bits, asym, G):
+    # Correlated calibration channels (GPTQ's case) and one dead channel.
+    seed = T + N + K + G
+    X = synth.correlated_activations(T, K, seed)
+    X[:, seed % K] = 0
+    W = synth.weights_with_outliers(N, K, seed + 1, seed + 2, seed + 3)
+    _say(f"gptq T={T} N={N} K={K} bits={bits} asym={asym} G={G}")
+    q, (packed, scales, zeros) = _gptq_gpu(X, W, bits, G, asym)
+    X64 = X.astype(np.float64)
+    r = O.gptq(X64, W, bits, G, asym)
+    # Both sides run the same fp64 recurrence in different summation orders
+    # (blocked Cholesky and triangular inverse against inverse-then-Cholesky;
+    # a deferred block update against the column loop): current weights agree
+    # to ~1e-13 relative, and a code can only differ where an fp64 weight sits
+    # that close to an fp32 rounding boundary (~1e-6 per decision).  A row
+    # that differs once then follows its own (equally valid) path, so allow at
+    # most 1% of rows to differ, and compare the objective.
+    eq = _row_equal(q, r)
+    lg, lr = O.reconstruction_loss(X64, W, q), O.reconstruction_loss(X64, W, r)
+    rtn = O.reconstruction_loss(X64, W, O.quantize(W, bits, G, asym))
+    _say(f"  rows identical {eq.sum()}/{N}; loss gpu {lg:.6e} oracle {lr:.6e} rtn {rtn:.6e}")
+    assert N - eq.sum() <= max(1, N // 100)
+    assert abs(lg / lr - 1) < 1e-3
+    assert lg < 0.8 * rtn
+    # the result is consumable by the GEMV as any quantize_pack output
+    x = synth.activations(1, K, seed + 4)
+    y = ops.gemv(gpu_f16(x), packed, scales, zeros, N, K, bits, G)
+    y_ref = O.gemm(x.astype(np.float64), O.dequantize(q))
+    assert O.rel_l2(host(y)[None, :], y_ref) < REL_L2
+
+
+def test_gptq_llama_q_proj_sampled_rows():
+    # Full size of one LLaMA-2-7B attention projection (N = K = 4096) on 2048
+    # calibration tokens.  GPTQ treats rows independently given U, so the
+    # oracle runs on sampled rows with the full X.
+    T, N, K = 2048, 4096, 4096
+    X = synth.correlated_activations(T, K, 6001)
+    W = synth.weights(N, K, 6002)
+    rows = np.concatenate([[0, 63, 64, N - 1], np.sort(np.random.default_rng(6003).choice(N, 20, replace=False))])
+    _say(f"gptq T={T} N={N} K={K} on {len(rows)} sampled rows")
+    q, _ = _gptq_gpu(X, W, 4, 128, True)
+    X64 = X.astype(np.float64)
+    r = O.gptq(X64, W[rows], 4, 128, True)
+    qs = O.Quantized(q.codes[rows], q.scales[rows], q.zeros[rows], 4, 128, True)
+    eq = _row_equal(qs, r)
+    lg, lr = O.reconstruction_loss(X64, W[rows], qs), O.reconstruction_loss(X64, W[rows], r)
+    rtn = O.reconstruction_loss(X64, W[rows], O.quantize(W[rows], 4, 128, True))
+    _say(f"  rows identical {eq.sum()}/{len(rows)}; loss gpu {lg:.6e} oracle {lr:.6e} rtn {rtn:.6e}")
+    assert len(rows) - eq.sum() <= 1
+    assert abs(lg / lr - 1) < 1e-3
+    assert lg < rtn

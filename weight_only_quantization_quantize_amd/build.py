@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libwoq.so")
 ARCH = os.environ.get("WOQ_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["woq_api.cpp", "quantize_pack.hip", "gemv.hip", "gemm.hip", "gemm_lds.hip", "dequantize.hip",
-           "awq_search.hip"]
+           "awq_search.hip", "gptq.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

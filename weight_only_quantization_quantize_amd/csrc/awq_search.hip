@@ -149,6 +149,14 @@ AwqLayout awq_layout(int64_t T, int64_t N, int64_t K, int bits, int G, bool asym
 
 }  // namespace
 
+hipError_t launch_dense_ref(const void* A, const void* B, int64_t M, int64_t N, int64_t K, float* Y,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(dense_ref_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64)), dim3(256), 0,
+                     stream, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), (int)M, (int)N, (int)K,
+                     Y);
+  return hipGetLastError();
+}
+
 size_t awq_search_workspace_bytes(int64_t T, int64_t N, int64_t K, int bits, int group_size, bool asymmetric) {
   return awq_layout(T, N, K, bits, group_size, asymmetric).total;
 }
@@ -171,10 +179,9 @@ hipError_t launch_awq_search(const void* X, const void* W, int64_t T, int64_t N,
 
   const unsigned kblocks = (unsigned)((K + 255) / 256);
   hipLaunchKernelGGL(channel_mean_kernel, dim3(kblocks), dim3(256), 0, stream, X16, (int)T, (int)K, m);
-  hipLaunchKernelGGL(dense_ref_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)((T + 63) / 64)), dim3(256), 0,
-                     stream, X16, W16, (int)T, (int)N, (int)K, yref);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if ((e = launch_dense_ref(X16, W16, T, N, K, yref, stream)) != hipSuccess) return e;
   for (int i = 0; i < n_grid; ++i) {
     hipLaunchKernelGGL(awq_scale_kernel, dim3(kblocks), dim3(256), 0, stream, m, (double)i / n_grid, (int)K, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -23,6 +23,7 @@
 // group statistic with lane shuffles; other group sizes use one workgroup per
 // group with an LDS reduction.  The pass is HBM-bound: 2 B read and b/8 B
 // written per weight.
+#include "rtn_rules.h"
 #include "woq_device.h"
 #include "woq_internal.h"
 
@@ -54,97 +55,6 @@ __device__ inline void load_chunk(const uint16_t* __restrict__ W, const float* _
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[4 * q + e] = w[4 * q + e] * sv[e];
     }
-  }
-}
-
-__device__ inline uint16_t f32_to_half_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
-
-// Scale (and zero point) of one group from its statistic.  For the
-// symmetric form `lo` is unused and `hi` is max|w|.
-template <int BITS, bool ASYM>
-struct GroupParams {
-  float S;        // the stored fp16 scale, widened exactly
-  int Z;          // zero point (symmetric: 2^(b-1))
-  uint16_t S16;   // fp16 bits of S
-  bool zero;      // S == 0: every code is Z
-};
-
-template <int BITS, bool ASYM>
-__device__ inline GroupParams<BITS, ASYM> group_params(float lo, float hi) {
-  GroupParams<BITS, ASYM> p;
-  if (!ASYM) {
-    const float qmax = (float)((1 << (BITS - 1)) - 1);
-    p.S16 = f32_to_half_bits(hi / qmax);
-    p.S = half_bits_to_f32(p.S16);
-    p.Z = 1 << (BITS - 1);
-    p.zero = (p.S == 0.0f);
-  } else {
-    const float qu = (float)((1 << BITS) - 1);
-    float r = hi - lo;
-    if (r == 0.0f) r = 1.0f;
-    p.S16 = f32_to_half_bits(r / qu);
-    p.S = half_bits_to_f32(p.S16);
-    p.zero = (p.S == 0.0f);
-    if (p.zero) {
-      p.Z = 0;
-    } else {
-      int z = (int)__builtin_rintf(-lo / p.S);
-      p.Z = z < 0 ? 0 : (z > (1 << BITS) - 1 ? (1 << BITS) - 1 : z);
-    }
-  }
-  return p;
-}
-
-template <int BITS, bool ASYM>
-__device__ inline void codes_of_chunk(const float (&w)[32], const GroupParams<BITS, ASYM>& p, uint32_t (&u)[32]) {
-  const int top = (1 << BITS) - 1;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    int v;
-    if (p.zero) {
-      v = p.Z;
-    } else {
-      int q = (int)__builtin_rintf(w[i] / p.S);
-      if (!ASYM) {
-        const int h = 1 << (BITS - 1);
-        q = q < -h ? -h : (q > h - 1 ? h - 1 : q);
-        v = q + h;
-      } else {
-        v = q + p.Z;
-        v = v < 0 ? 0 : (v > top ? top : v);
-      }
-    }
-    u[i] = (uint32_t)v;
-  }
-}
-
-template <int BITS>
-__device__ inline void store_chunk(uint8_t* __restrict__ packed, int64_t n, int K, int kc, const uint32_t (&u)[32]) {
-  if (BITS == 4) {
-    u32x4_t out;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) word |= u[8 * j + 2 * t + h] << (16 * h + 4 * t);
-      out[j] = word;
-    }
-    *reinterpret_cast<u32x4_t*>(packed + n * (int64_t)(K / 2) + (int64_t)kc * 16) = out;
-  } else {
-    uint32_t w0 = 0, w1 = 0, w2 = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int t = i >> 1, h = i & 1;
-      const uint32_t lo = (u[i] & 3u) << (16 * h + 2 * (t & 7));
-      if (t < 8) w0 |= lo; else w1 |= lo;
-      w2 |= ((u[i] >> 2) & 1u) << (16 * h + t);
-    }
-    uint32_t* dst = reinterpret_cast<uint32_t*>(packed + n * (int64_t)(3 * K / 8) + (int64_t)kc * 12);
-    dst[0] = w0;
-    dst[1] = w1;
-    dst[2] = w2;
   }
 }
 

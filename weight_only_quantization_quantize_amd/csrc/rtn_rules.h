@@ -1,0 +1,113 @@
+// Round-to-nearest rules shared by every kernel that decides codes: the
+// group scale / zero point and the code of one weight, each decision one
+// correctly rounded binary32 operation (IEEE division, rintf = round half to
+// even, fp32 -> fp16 round-to-nearest-even with subnormals), and the layout-v1
+// store of a 32-code chunk.
+//
+//   symmetric : S = f16(max|w| / (2^(b-1)-1)), u = clip(rne(w/S), -2^(b-1), 2^(b-1)-1) + 2^(b-1)
+//   asymmetric: r = max-min (1 if 0), S = f16(r / (2^b-1)),
+//               Z = clip(rne(-min/S), 0, 2^b-1), u = clip(rne(w/S) + Z, 0, 2^b-1)
+//
+// ("Quantising Large Language Models for Efficient Inference", section
+// "Post-training methods for 4-bit weights"; "CMU 11-868 L19-L20 Model
+// Quantization", section "absmax and zero-point"; "LLM Quantization: 160GB
+// Model on a Laptop", sections "Symmetric Quantization" and "Asymmetric
+// Quantization".)  None of these has a multiply-add for the compiler to
+// contract.
+#pragma once
+
+#include "woq_device.h"
+
+namespace woq {
+
+__device__ inline uint16_t f32_to_half_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Scale (and zero point) of one group from its statistic.  For the
+// symmetric form `lo` is unused and `hi` is max|w|.
+template <int BITS, bool ASYM>
+struct GroupParams {
+  float S;        // the stored fp16 scale, widened exactly
+  int Z;          // zero point (symmetric: 2^(b-1))
+  uint16_t S16;   // fp16 bits of S
+  bool zero;      // S == 0: every code is Z
+};
+
+template <int BITS, bool ASYM>
+__device__ inline GroupParams<BITS, ASYM> group_params(float lo, float hi) {
+  GroupParams<BITS, ASYM> p;
+  if (!ASYM) {
+    const float qmax = (float)((1 << (BITS - 1)) - 1);
+    p.S16 = f32_to_half_bits(hi / qmax);
+    p.S = half_bits_to_f32(p.S16);
+    p.Z = 1 << (BITS - 1);
+    p.zero = (p.S == 0.0f);
+  } else {
+    const float qu = (float)((1 << BITS) - 1);
+    float r = hi - lo;
+    if (r == 0.0f) r = 1.0f;
+    p.S16 = f32_to_half_bits(r / qu);
+    p.S = half_bits_to_f32(p.S16);
+    p.zero = (p.S == 0.0f);
+    if (p.zero) {
+      p.Z = 0;
+    } else {
+      int z = (int)__builtin_rintf(-lo / p.S);
+      p.Z = z < 0 ? 0 : (z > (1 << BITS) - 1 ? (1 << BITS) - 1 : z);
+    }
+  }
+  return p;
+}
+
+// Code of one weight: u = clip(rne(w / S), ...) (+ 2^(b-1) or + Z).
+template <int BITS, bool ASYM>
+__device__ inline uint32_t code_of(float w, const GroupParams<BITS, ASYM>& p) {
+  if (p.zero) return (uint32_t)p.Z;
+  int q = (int)__builtin_rintf(w / p.S);
+  if (!ASYM) {
+    const int h = 1 << (BITS - 1);
+    q = q < -h ? -h : (q > h - 1 ? h - 1 : q);
+    return (uint32_t)(q + h);
+  }
+  const int top = (1 << BITS) - 1;
+  const int v = q + p.Z;
+  return (uint32_t)(v < 0 ? 0 : (v > top ? top : v));
+}
+
+template <int BITS, bool ASYM>
+__device__ inline void codes_of_chunk(const float (&w)[32], const GroupParams<BITS, ASYM>& p, uint32_t (&u)[32]) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) u[i] = code_of<BITS, ASYM>(w[i], p);
+}
+
+template <int BITS>
+__device__ inline void store_chunk(uint8_t* __restrict__ packed, int64_t n, int K, int kc, const uint32_t (&u)[32]) {
+  if (BITS == 4) {
+    u32x4_t out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) word |= u[8 * j + 2 * t + h] << (16 * h + 4 * t);
+      out[j] = word;
+    }
+    *reinterpret_cast<u32x4_t*>(packed + n * (int64_t)(K / 2) + (int64_t)kc * 16) = out;
+  } else {
+    uint32_t w0 = 0, w1 = 0, w2 = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int t = i >> 1, h = i & 1;
+      const uint32_t lo = (u[i] & 3u) << (16 * h + 2 * (t & 7));
+      if (t < 8) w0 |= lo; else w1 |= lo;
+      w2 |= ((u[i] >> 2) & 1u) << (16 * h + t);
+    }
+    uint32_t* dst = reinterpret_cast<uint32_t*>(packed + n * (int64_t)(3 * K / 8) + (int64_t)kc * 12);
+    dst[0] = w0;
+    dst[1] = w1;
+    dst[2] = w2;
+  }
+}
+
+
+}  // namespace woq

@@ -93,6 +93,20 @@ woq_status from_hip(hipError_t e, const char* what) {
     return fail(WOQ_ERR_INTERNAL, "internal error: unknown exception");      \
   }
 
+// GPTQ runs 128-column blocks whose groups either split a block evenly or
+// cover whole blocks; the factorization uses 64-wide panels.
+woq_status check_gptq(int64_t T, int64_t N, int64_t K, int32_t bits, int32_t group_size) {
+  WOQ_TRY(check_qparams(N, K, bits, group_size));
+  if (T < 1) return fail(WOQ_ERR_INVALID_ARGUMENT, "T must be >= 1 (got %lld)", (long long)T);
+  if (K % 128 != 0) return fail(WOQ_ERR_UNSUPPORTED, "gptq needs K %% 128 == 0 (got K=%lld)", (long long)K);
+  if (128 % group_size != 0 && group_size % 128 != 0)
+    return fail(WOQ_ERR_UNSUPPORTED, "gptq needs group_size dividing 128 or a multiple of 128 (got %d)", group_size);
+  if (K > 32768 || T > INT32_MAX || N > ((int64_t)1 << 31))
+    return fail(WOQ_ERR_UNSUPPORTED, "gptq sizes too large for this build (T=%lld, N=%lld, K=%lld)", (long long)T,
+                (long long)N, (long long)K);
+  return WOQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,6 +244,34 @@ woq_status woq_awq_search(const void* X, const void* W, int64_t T, int64_t N, in
   return from_hip(woq::launch_awq_search(X, W, T, N, K, bits, group_size, asymmetric != 0, n_grid, losses,
                                          best_scale, best_index, workspace, static_cast<hipStream_t>(stream)),
                   "awq_search launch");
+  WOQ_GUARD_END
+}
+
+size_t woq_gptq_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t bits, int32_t group_size) {
+  if (check_gptq(T, N, K, bits, group_size) != WOQ_OK) return 0;
+  return woq::gptq_workspace_bytes(T, N, K);
+}
+
+woq_status woq_gptq_quantize_pack(const void* X, const void* W, int64_t T, int64_t N, int64_t K, int32_t bits,
+                                  int32_t group_size, int32_t asymmetric, double damp, void* packed, void* scales,
+                                  void* zeros, void* workspace, size_t workspace_bytes, void* stream) {
+  WOQ_GUARD_BEGIN
+  WOQ_TRY(check_gptq(T, N, K, bits, group_size));
+  if (!(damp > 0.0) || !(damp <= 1e6)) return fail(WOQ_ERR_INVALID_ARGUMENT, "damp must be in (0, 1e6] (got %g)", damp);
+  if (!X || !W) return fail(WOQ_ERR_INVALID_ARGUMENT, "X and W must not be NULL");
+  if (!aligned(X, 16) || !aligned(W, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "X and W must be 16-byte aligned");
+  if (!packed || !aligned(packed, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "packed must be non-NULL, 16-byte aligned");
+  if (!scales || !aligned(scales, 2)) return fail(WOQ_ERR_INVALID_ARGUMENT, "scales must be non-NULL, 2-byte aligned");
+  if (asymmetric && (!zeros || !aligned(zeros, 2)))
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "zeros must be non-NULL and 2-byte aligned when asymmetric");
+  const size_t need = woq::gptq_workspace_bytes(T, N, K);
+  if (!workspace || !aligned(workspace, 256))
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "workspace too small (%zu bytes, need %zu)", workspace_bytes, need);
+  return from_hip(woq::launch_gptq(X, W, T, N, K, bits, group_size, asymmetric != 0, damp, packed, scales,
+                                   asymmetric ? zeros : nullptr, workspace, static_cast<hipStream_t>(stream)),
+                  "gptq launch");
   WOQ_GUARD_END
 }
 

@@ -35,6 +35,18 @@ hipError_t launch_awq_search(const void* X, const void* W, int64_t T, int64_t N,
                              int group_size, bool asymmetric, int n_grid, double* losses, float* best_scale,
                              int32_t* best_index, void* workspace, hipStream_t stream);
 
+// Y[m, n] = sum_k A[m, k] B[n, k] in fp32 for fp16 A [M, K], B [N, K]
+// (K % 16 == 0): the dense MFMA product the AWQ and GPTQ passes use for
+// reference outputs and Hessians.
+hipError_t launch_dense_ref(const void* A, const void* B, int64_t M, int64_t N, int64_t K, float* Y,
+                            hipStream_t stream);
+
+// GPTQ into layout v1 (scratch in the caller's workspace).
+size_t gptq_workspace_bytes(int64_t T, int64_t N, int64_t K);
+hipError_t launch_gptq(const void* X, const void* W, int64_t T, int64_t N, int64_t K, int bits, int group_size,
+                       bool asymmetric, double damp, void* packed, void* scales, void* zeros, void* workspace,
+                       hipStream_t stream);
+
 // Dequantize to fp32 (test aid).
 hipError_t launch_dequantize(const void* packed, const void* scales, const void* zeros, int64_t N,
                              int64_t K, int bits, int group_size, bool asymmetric, float* out,

@@ -215,3 +215,34 @@ def awq_search(
                    _stream(X))
     _lib.check(st, "woq_awq_search")
     return losses, best_scale, best_index
+
+
+def gptq(
+    X: torch.Tensor,
+    W: torch.Tensor,
+    bits: int = 4,
+    group_size: int = 128,
+    asymmetric: bool = True,
+    damp: float = 0.01,
+):
+    """GPTQ of fp16 W [N, K] on fp16 calibration activations X [T, K] ->
+    (packed, scales, zeros | None) in the same layout as quantize_pack.  The
+    workspace is allocated here (PyTorch memory) and released on return."""
+    if X.dtype != torch.float16 or W.dtype != torch.float16 or X.dim() != 2 or W.dim() != 2:
+        raise ValueError("X and W must be 2-D float16 tensors")
+    T, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("X and W must share K")
+    nbytes = int(_lib.call("woq_gptq_workspace_bytes", T, N, K, bits, group_size))
+    if nbytes == 0:
+        raise ValueError("unsupported shape or quantizer for gptq")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=X.device)
+    packed = torch.empty((N, K * bits // 8), dtype=torch.uint8, device=W.device)
+    scales = torch.empty((N, K // group_size), dtype=torch.float16, device=W.device)
+    zeros = torch.empty_like(scales) if asymmetric else None
+    _require_gpu(X, W, ws, packed, scales, zeros)
+    st = _lib.call("woq_gptq_quantize_pack", X.data_ptr(), W.data_ptr(), T, N, K, bits, group_size, int(asymmetric),
+                   float(damp), packed.data_ptr(), scales.data_ptr(), _ptr(zeros), ws.data_ptr(), nbytes, _stream(X))
+    _lib.check(st, "woq_gptq_quantize_pack")
+    return packed, scales, zeros

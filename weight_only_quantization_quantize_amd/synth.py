@@ -86,6 +86,17 @@ def activations_f32(
     return x
 
 
+def correlated_activations(T: int, K: int, seed: int, rank: int = 16, noise: float = 0.3) -> np.ndarray:
+    """fp16 [T, K] calibration activations with correlated channels: a
+    rank-``rank`` mixture of N(0, 1) draws plus N(0, noise^2) noise (a stand-in
+    for real hidden states, whose channels are far from independent)."""
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal(size=(T, rank))
+    a = rng.standard_normal(size=(rank, K))
+    x = z @ a + noise * rng.standard_normal(size=(T, K))
+    return x.astype(np.float32).astype(np.float16)
+
+
 def to_f16(x32: np.ndarray) -> np.ndarray:
     return np.asarray(x32, dtype=np.float32).astype(np.float16)
 

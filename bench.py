@@ -343,6 +343,25 @@ def time_rows(torch, ops, synth):
                                  "loss_best_over_rtn": float(f"{L[b] / L[0]:.4g}")}
     del Xc, Wq
 
+    # GPTQ of the q_proj shape (N = K = 4096) on 2048 correlated calibration
+    # tokens, 4-bit asym g128; the layer objective ||X (W - w_hat)^T||^2 is
+    # compared with RTN's (fp32 products on the device, fp64 sums).
+    T, N, K = 2048, 4096, 4096
+    Xg = torch.from_numpy(synth.correlated_activations(T, K, 6001)).to(dev)
+    Wg = torch.from_numpy(synth.weights(N, K, 6002)).to(dev)
+    ops.gptq(Xg, Wg, 4, 128, True)
+    torch.cuda.synchronize()
+    us = burst_us(torch, [lambda: ops.gptq(Xg, Wg, 4, 128, True)], reps=3)
+
+    def layer_loss(q):
+        D = Wg.float() - ops.dequantize(q[0], q[1], q[2], N, K, 4, 128)
+        return float(((Xg.float() @ D.T).double() ** 2).sum())
+
+    lg, lr = layer_loss(ops.gptq(Xg, Wg, 4, 128, True)), layer_loss(ops.quantize_pack(Wg, 4, 128, True))
+    rows["gptq_q_proj"] = {"T": T, "N": N, "K": K, "ms": round(us / 1e3, 3),
+                           "loss_gptq_over_rtn": float(f"{lg / lr:.4g}")}
+    del Xg, Wg
+
     # quantize_pack over 32 layers of the LLaMA-2-7B linear shapes (weights
     # generated on the device, seed 5100 + layer), 4-bit asym g128.
     shapes = [(N, K) for _, N, K in synth.LLAMA7B_LINEARS]

@@ -240,11 +240,11 @@ def test_gptq_unsupported(lib, kw, needle):
 
 
 def test_gptq_workspace_size(lib):
-    # M and Y (K x K fp64), the fp64 working weights, 128 fp64 errors per row
+    # M and Y (K x K fp64), the inverse's temporary (K^2/4 fp64), the fp64 working weights, 128 fp64 errors per row
     # (rows padded to 64), dead-channel flags: all 256-byte padded
     T, N, K = 100, 70, 256
     need = lib.woq_gptq_workspace_bytes(T, N, K, 4, 128)
-    parts = [8 * K * K, 8 * K * K, 8 * N * K, 8 * 128 * 128, K]
+    parts = [8 * K * K, 8 * K * K, 8 * K * K // 4, 8 * N * K, 8 * 128 * 128, K]
     assert need == sum((p + 255) // 256 * 256 for p in parts)
     assert lib.woq_gptq_workspace_bytes(0, N, K, 4, 128) == 0
     assert lib.woq_gptq_workspace_bytes(T, N, 96, 4, 32) == 0

@@ -502,7 +502,7 @@ def test_gptq_with_a_diagonal_hessian_is_rtn(bits, asym, G, N, K):
 
 @pytest.mark.parametrize("T,N,K,bits,asym,G", [(192, 100, 256, 4, True, 128), (250, 70, 384, 3, False, 32),
                                                (128, 64, 512, 4, False, 64), (200, 65, 256, 4, True, 256),
-                                               (301, 48, 384, 3, True, 384)])
+                                               (301, 48, 384, 3, True, 384), (160, 40, 640, 4, True, 128)])
 def test_gptq_matches_oracle(T, N, K, bits, asym, G):
     # Correlated calibration channels (GPTQ's case) and one dead channel.
     seed = T + N + K + G

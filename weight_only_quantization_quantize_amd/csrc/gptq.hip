@@ -19,13 +19,13 @@
 //   1. M = J H J (J reverses the channel order), the lower triangle from a
 //      tiled fp64 product over the tokens; damping and dead channels on its
 //      diagonal.
-//   2. Blocked Cholesky M = L L^T (64-wide panels: a one-workgroup diagonal
-//      factorization, a triangular solve of the panel below it and a
-//      symmetric update of the trailing lower triangle).
-//   3. Y = L^-1 by block rows (each block a product over the blocks already
-//      inverted, then a solve with the diagonal block).
+//   2. Blocked Cholesky M = L L^T (64-wide panels: a one-wave factorization
+//      and inversion of the diagonal block, the panel below it multiplied by
+//      that inverse's transpose, and a symmetric update of the trailing lower
+//      triangle).
+//   3. Y = L^-1 by recursive doubling over the diagonal blocks.
 //   4. U = J Y J (upper, since J H^-1 J = Y^T Y), written over M.
-//   5. Columns in blocks of 128: one wave per 64 rows quantizes the block
+//   5. Columns in blocks of 128: a workgroup per 64 rows quantizes the block
 //      column by column in LDS, applying the updates inside the block at once
 //      and saving the scaled errors E; then one tiled product applies
 //      W[:, later] -= E U[block, later] to every later column.
@@ -130,53 +130,77 @@ __global__ __launch_bounds__(256) void damp_kernel(double* __restrict__ M, int64
   }
 }
 
-// Cholesky of the diagonal block of panel p, in LDS, in place in M (lower
-// triangle; the strictly upper part of the block is set to 0).
-__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ M, int64_t K, int p) {
-  __shared__ double a[kPanel][kPitch];
+// Diagonal block of panel p (one wave): Cholesky factor L[P, P] in place in
+// M (strictly upper part set to 0) and its inverse into Y[P, P].
+//  - Factor, right-looking, lane r holding row r in registers: for column j,
+//    L[j][j] = sqrt(a[j][j]); L[r][j] = a[r][j] / L[j][j]; then
+//    a[r][c] -= L[r][j] L[c][j] for c > j (lanes r < c update entries that
+//    are never read), the pivot and the column published through LDS.
+//  - Inverse, lane c solving L z = e_c, right-looking over rows with the
+//    columns of L read as LDS broadcasts: z_r = s_r * (1 / L[r][r]), then
+//    s_r' -= L[r'][r] z_r for r' > r (z_r = 0 for r < c exactly).
+__global__ __launch_bounds__(64) void potrf_inv_kernel(double* __restrict__ M, double* __restrict__ Y, int64_t K,
+                                                       int p) {
+  __shared__ double col[kPanel], rd[kPanel];
+  __shared__ double lt[kPanel][kPitch];  // lt[q][r] = L[r][q]
   const int64_t P0 = (int64_t)p * kPanel;
-  const int tid = threadIdx.x;
-  for (int idx = tid; idx < kPanel * kPanel; idx += 256) {
-    const int r = idx >> 6, c = idx & 63;
-    a[r][c] = c <= r ? M[(P0 + r) * K + P0 + c] : 0.0;
+  const int lane = threadIdx.x;
+  double a[kPanel];
+#pragma unroll
+  for (int c = 0; c < kPanel; ++c) a[c] = c <= lane ? M[(P0 + lane) * K + P0 + c] : 0.0;
+#pragma unroll
+  for (int j = 0; j < kPanel; ++j) {
+    if (lane == j) col[j] = __builtin_sqrt(a[j]);
+    __syncthreads();
+    const double d = col[j];
+    const double l = lane == j ? d : a[j] / d;
+    a[j] = lane >= j ? l : 0.0;
+    __syncthreads();
+    col[lane] = l;
+    __syncthreads();
+#pragma unroll
+    for (int c = j + 1; c < kPanel; ++c) a[c] = __builtin_fma(-l, col[c], a[c]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int c = 0; c < kPanel; ++c) {
+    const double v = c <= lane ? a[c] : 0.0;
+    lt[c][lane] = v;
+    M[(P0 + lane) * K + P0 + c] = v;
   }
   __syncthreads();
-  for (int j = 0; j < kPanel; ++j) {
-    if (tid == 0) a[j][j] = __builtin_sqrt(a[j][j]);
-    __syncthreads();
-    if (tid > j && tid < kPanel) a[tid][j] /= a[j][j];
-    __syncthreads();
-    const int m = kPanel - 1 - j;
-    for (int idx = tid; idx < m * m; idx += 256) {
-      const int r = j + 1 + idx / m, c = j + 1 + idx % m;
-      if (c <= r) a[r][c] = __builtin_fma(-a[r][j], a[c][j], a[r][c]);
-    }
-    __syncthreads();
+  rd[lane] = 1.0 / lt[lane][lane];
+  __syncthreads();
+  double z[kPanel];
+#pragma unroll
+  for (int r = 0; r < kPanel; ++r) z[r] = r == lane ? 1.0 : 0.0;
+#pragma unroll
+  for (int r = 0; r < kPanel; ++r) {
+    z[r] = z[r] * rd[r];
+#pragma unroll
+    for (int q = r + 1; q < kPanel; ++q) z[q] = __builtin_fma(-lt[r][q], z[r], z[q]);
   }
-  for (int idx = tid; idx < kPanel * kPanel; idx += 256) {
-    const int r = idx >> 6, c = idx & 63;
-    M[(P0 + r) * K + P0 + c] = a[r][c];
-  }
+#pragma unroll
+  for (int r = 0; r < kPanel; ++r) Y[(P0 + r) * K + P0 + lane] = z[r];
 }
 
-// Panel below the diagonal block: L[I, P] = A[I, P] L[P, P]^-T, block row
-// I = p + 1 + blockIdx.x, one lane per row.
-__global__ __launch_bounds__(64) void trsm_panel_kernel(double* __restrict__ M, int64_t K, int p) {
-  __shared__ double l[kPanel][kPitch], v[kPanel][kPitch];
+// Panel below the diagonal block: L[I, P] = A[I, P] L[P, P]^-T as a tile
+// product with the inverse from potrf_inv_kernel, block row
+// I = p + 1 + blockIdx.x, in place (each workgroup reads its rows completely
+// before writing them).
+__global__ __launch_bounds__(256) void trsm_panel_kernel(double* __restrict__ M, const double* __restrict__ Y,
+                                                         int64_t K, int p) {
+  __shared__ double As[kTileK][kPitch], Bs[kTileK][kPitch];
   const int64_t P0 = (int64_t)p * kPanel, I0 = (int64_t)(p + 1 + blockIdx.x) * kPanel;
-  const int lane = threadIdx.x;
-  for (int r = 0; r < kPanel; ++r) {
-    l[r][lane] = M[(P0 + r) * K + P0 + lane];
-    v[lane][r] = M[(I0 + r) * K + P0 + lane];
-  }
-  __syncthreads();
-  for (int c = 0; c < kPanel; ++c) {
-    double s = v[c][lane];
-    for (int q = 0; q < c; ++q) s = __builtin_fma(-v[q][lane], l[c][q], s);
-    v[c][lane] = s / l[c][c];
-  }
-  __syncthreads();
-  for (int r = 0; r < kPanel; ++r) M[(I0 + r) * K + P0 + lane] = v[lane][r];
+  double acc[4][4];
+  zero_acc(acc);
+  tile_product<true, true>([&](int i, int q) { return M[(I0 + i) * K + P0 + q]; },
+                           [&](int q, int j) { return Y[(P0 + j) * K + P0 + q]; }, kPanel, acc, As, Bs);
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) M[(I0 + tr + 16 * r) * K + P0 + tc + 16 * c] = acc[r][c];
 }
 
 // Trailing update of the lower blocks (I, J), p < J <= I:
@@ -200,45 +224,61 @@ __global__ __launch_bounds__(256) void syrk_trailing_kernel(double* __restrict__
     }
 }
 
-// Block row i of Y = L^-1: for block column j = blockIdx.x <= i,
-// R = (j == i ? I : -sum_{m=j}^{i-1} L[i, m] Y[m, j]) and Y[i, j] = L[i, i]^-1 R.
-__global__ __launch_bounds__(256) void trtri_row_kernel(const double* __restrict__ M, double* __restrict__ Y,
-                                                        int64_t K, int i) {
+// Y = L^-1 by recursive doubling.  The 64 x 64 diagonal blocks are inverted
+// with the factorization (potrf_inv_kernel); then, for s = 64, 128, ... while s < K, each diagonal
+// segment [2 s z, min(2 s (z + 1), K)) = [[A, 0], [B, C]] with A of size s and
+// C of size sc = min(s, K - 2 s z - s) > 0 (A and C already inverted) gets its
+// lower-left block -C^-1 B A^-1, as two batched products through a
+// temporary (pair z's s x sc product at offset z s^2; at most s (K - s) <=
+// K^2 / 4 doubles).
+
+// Level s, first product: Tmp[p] = B_p A_p^-1 for pair p = blockIdx.z (pair
+// origin o = 2 s p; rows past sc and pairs with sc <= 0 return at once):
+// B_p = L[o+s .., o ..] (sc x s), A_p^-1 = Y[o .., o ..] (s x s, lower
+// triangular, so the inner index starts at the tile's first column).
+__global__ __launch_bounds__(256) void pair_left_kernel(const double* __restrict__ M, const double* __restrict__ Y,
+                                                        int64_t K, int64_t s, double* __restrict__ Tmp) {
   __shared__ double As[kTileK][kPitch], Bs[kTileK][kPitch];
-  __shared__ double l[kPanel][kPitch], rs[kPanel][kPitch];
-  const int j = blockIdx.x;
-  const int64_t I0 = (int64_t)i * kPanel, J0 = (int64_t)j * kPanel;
-  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+  const int64_t o = 2 * s * blockIdx.z, r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int64_t sc = K - o - s < s ? K - o - s : s;
+  if (r0 >= sc) return;
   double acc[4][4];
   zero_acc(acc);
-  if (j < i)
-    tile_product<true, false>([&](int r, int q) { return M[(I0 + r) * K + J0 + q]; },
-                              [&](int q, int c) { return Y[(J0 + q) * K + J0 + c]; }, (i - j) * kPanel, acc, As, Bs);
+  tile_product<true, false>([&](int i, int q) { return M[(o + s + r0 + i) * K + o + c0 + q]; },
+                            [&](int q, int j) { return Y[(o + c0 + q) * K + o + c0 + j]; }, (int)(s - c0), acc, As,
+                            Bs);
+  double* T = Tmp + (int64_t)blockIdx.z * s * s;
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int rr = tr + 16 * r, cc = tc + 16 * c;
-      rs[rr][cc] = j == i ? (rr == cc ? 1.0 : 0.0) : -acc[r][c];
-    }
-  for (int idx = tid; idx < kPanel * kPanel; idx += 256) {
-    const int r = idx >> 6, c = idx & 63;
-    l[r][c] = M[(I0 + r) * K + I0 + c];
-  }
-  __syncthreads();
-  if (tid < kPanel) {
-    const int c = tid;
-    for (int r = 0; r < kPanel; ++r) {
-      double s = rs[r][c];
-      for (int q = 0; q < r; ++q) s = __builtin_fma(-l[r][q], rs[q][c], s);
-      rs[r][c] = s / l[r][r];
-    }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < kPanel * kPanel; idx += 256) {
-    const int r = idx >> 6, c = idx & 63;
-    Y[(I0 + r) * K + J0 + c] = rs[r][c];
-  }
+    for (int c = 0; c < 4; ++c) T[(r0 + tr + 16 * r) * s + c0 + tc + 16 * c] = acc[r][c];
+}
+
+// Level s, second product: Y[o+s .., o ..] = -C_p^-1 Tmp[p], C_p^-1 =
+// Y[o+s .., o+s ..] (lower triangular: the inner index stops after the tile's
+// last row).
+__global__ __launch_bounds__(256) void pair_right_kernel(double* __restrict__ Y, int64_t K, int64_t s,
+                                                         const double* __restrict__ Tmp) {
+  __shared__ double As[kTileK][kPitch], Bs[kTileK][kPitch];
+  const int64_t o = 2 * s * blockIdx.z, r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int64_t sc = K - o - s < s ? K - o - s : s;
+  if (r0 >= sc) return;
+  const double* T = Tmp + (int64_t)blockIdx.z * s * s;
+  double acc[4][4];
+  zero_acc(acc);
+  tile_product<true, false>([&](int i, int q) { return Y[(o + s + r0 + i) * K + o + s + q]; },
+                            [&](int q, int j) { return T[q * s + c0 + j]; }, (int)(r0 + 64), acc, As, Bs);
+  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) Y[(o + s + r0 + tr + 16 * r) * K + o + c0 + tc + 16 * c] = -acc[r][c];
+}
+
+// Zero fill (the upper blocks of Y are read as zeros by the products).
+__global__ __launch_bounds__(256) void zero_kernel(double* __restrict__ p, int64_t count) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < count; e += (int64_t)gridDim.x * 256) p[e] = 0.0;
 }
 
 // U[a][b] = Y[K-1-a][K-1-b] for a <= b, 0 below the diagonal.
@@ -299,28 +339,43 @@ __global__ __launch_bounds__(256) void wide_group_params_kernel(const double* __
   }
 }
 
-// One 128-column block of 64 rows, one wave, one lane per row.  The rows'
-// block values live in LDS as w[c][lane]; U[block, block] is read with
-// wave-uniform addresses.  Writes the codes (layout v1), the parameters of
-// the groups that start in the block (group_size 32 or 64 or 128) and the
-// scaled errors Et[c][n].
+// One 128-column block of 64 rows on eight waves.  Wave v keeps columns
+// [16 v, 16 v + 16) of row `lane` in registers; U[block, block] sits in LDS
+// (its zeros below the diagonal included).  Column c belongs to wave c / 16,
+// which quantizes it for its 64 rows and publishes the scaled errors through
+// LDS (double-buffered, one barrier per column); then every wave subtracts
+// err * U[c][j] from its 16 columns.  Columns j < c see U[c][j] = 0 and
+// column c itself becomes w_hat, neither of which is read again.  Group
+// statistics (group size 32 or 64) combine eight per-wave partials in a
+// fixed order.  Writes the codes (layout v1), the parameters of the groups
+// that start in the block and the scaled errors Et[c][n].
+constexpr int kBlockWaves = 8;
+constexpr int kOwn = kColBlock / kBlockWaves;
+
 template <int BITS, bool ASYM>
-__global__ __launch_bounds__(64) void gptq_block_kernel(const double* __restrict__ W64, const double* __restrict__ U,
-                                                        int64_t N, int64_t K, int G, int64_t c0, int64_t Npad,
-                                                        uint8_t* __restrict__ packed, uint16_t* __restrict__ scales,
-                                                        uint16_t* __restrict__ zeros, double* __restrict__ Et) {
-  __shared__ double w[kColBlock][kPitch];
+__global__ __launch_bounds__(64 * kBlockWaves) void gptq_block_kernel(
+    const double* __restrict__ W64, const double* __restrict__ U, int64_t N, int64_t K, int G, int64_t c0,
+    int64_t Npad, uint8_t* __restrict__ packed, uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros,
+    double* __restrict__ Et) {
+  __shared__ double ub[kColBlock][kColBlock];
+  __shared__ double errs[2][64];
+  __shared__ float stat[2][kBlockWaves][64];
   __shared__ uint8_t us[kColBlock][64];
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t n0 = (int64_t)blockIdx.x * 64, n = n0 + lane;
-  for (int r = 0; r < 64; ++r) {
-    const int64_t nr = n0 + r < N ? n0 + r : N - 1;
-    w[lane][r] = W64[nr * K + c0 + lane];
-    w[lane + 64][r] = W64[nr * K + c0 + lane + 64];
-  }
-  __syncthreads();
-  const int64_t ng = K / G;
   const int64_t nc = n < N ? n : N - 1;
+  for (int idx = tid; idx < kColBlock * kColBlock; idx += 64 * kBlockWaves) {
+    const int c = idx >> 7, j = idx & (kColBlock - 1);
+    ub[c][j] = U[(c0 + c) * K + c0 + j];
+  }
+  double w[kOwn];
+  const double* src = W64 + nc * K + c0 + kOwn * wave;
+#pragma unroll
+  for (int q = 0; q < kOwn; ++q) w[q] = src[q];
+  __syncthreads();
+
+  const int64_t ng = K / G;
   GroupParams<BITS, ASYM> p{};
   if (G >= kColBlock) {
     const int64_t gi = nc * ng + c0 / G;
@@ -329,33 +384,55 @@ __global__ __launch_bounds__(64) void gptq_block_kernel(const double* __restrict
     p.Z = ASYM ? (int)half_bits_to_f32(zeros[gi]) : 1 << (BITS - 1);
     p.zero = p.S == 0.0f;
   }
-  const double* Ub = U + c0 * K + c0;
   for (int c = 0; c < kColBlock; ++c) {
+    const int owner = c / kOwn, slot = c % kOwn;
     if (G < kColBlock && c % G == 0) {
-      float lo = (float)w[c][lane], hi = ASYM ? lo : 0.0f;
-      for (int q = 0; q < G; ++q) fold_stat<ASYM>((float)w[c + q][lane], lo, hi);
+      float lo = __builtin_huge_valf(), hi = ASYM ? -__builtin_huge_valf() : 0.0f;
+#pragma unroll
+      for (int q = 0; q < kOwn; ++q) {
+        const int j = kOwn * wave + q;
+        if (j >= c && j < c + G) fold_stat<ASYM>((float)w[q], lo, hi);
+      }
+      stat[0][wave][lane] = lo;
+      stat[1][wave][lane] = hi;
+      __syncthreads();
+      lo = stat[0][0][lane];
+      hi = stat[1][0][lane];
+#pragma unroll
+      for (int v = 1; v < kBlockWaves; ++v) {
+        lo = fminf(lo, stat[0][v][lane]);
+        hi = fmaxf(hi, stat[1][v][lane]);
+      }
       p = group_params<BITS, ASYM>(lo, hi);
-      if (n < N) {
+      if (wave == owner && n < N) {
         const int64_t gi = n * ng + (c0 + c) / G;
         scales[gi] = p.S16;
         if (ASYM) zeros[gi] = f32_to_half_bits((float)p.Z);
       }
     }
-    const double wc = w[c][lane];
-    const uint32_t u = code_of<BITS, ASYM>((float)wc, p);
-    us[c][lane] = (uint8_t)u;
-    const double what = ((double)(int)u - (double)p.Z) * (double)p.S;
-    const double err = (wc - what) / Ub[(int64_t)c * K + c];
-    Et[(int64_t)c * Npad + n] = err;
-    for (int j = c + 1; j < kColBlock; ++j) w[j][lane] = __builtin_fma(-err, Ub[(int64_t)c * K + j], w[j][lane]);
+    if (wave == owner) {
+      double wc = w[0];
+#pragma unroll
+      for (int q = 1; q < kOwn; ++q) wc = slot == q ? w[q] : wc;
+      const uint32_t u = code_of<BITS, ASYM>((float)wc, p);
+      const double what = ((double)(int)u - (double)p.Z) * (double)p.S;
+      const double err = (wc - what) / ub[c][c];
+      errs[c & 1][lane] = err;
+      us[c][lane] = (uint8_t)u;
+      Et[(int64_t)c * Npad + n] = err;
+    }
+    __syncthreads();
+    const double err = errs[c & 1][lane];
+    const double* urow = &ub[c][kOwn * wave];
+#pragma unroll
+    for (int q = 0; q < kOwn; ++q) w[q] = __builtin_fma(-err, urow[q], w[q]);
   }
   if (n >= N) return;
+  if (wave < kColBlock / 32) {
+    uint32_t uc[32];
 #pragma unroll
-  for (int kc = 0; kc < kColBlock / 32; ++kc) {
-    uint32_t u[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) u[i] = us[32 * kc + i][lane];
-    store_chunk<BITS>(packed, n, (int)K, (int)(c0 / 32 + kc), u);
+    for (int i = 0; i < 32; ++i) uc[i] = us[32 * wave + i][lane];
+    store_chunk<BITS>(packed, n, (int)K, (int)(c0 / 32 + wave), uc);
   }
 }
 
@@ -386,7 +463,7 @@ __global__ __launch_bounds__(256) void gptq_update_kernel(double* __restrict__ W
 constexpr size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct GptqLayout {
-  size_t m, y, w64, et, dead, total;
+  size_t m, y, tmp, w64, et, dead, total;
 };
 
 GptqLayout gptq_layout(int64_t N, int64_t K) {
@@ -400,6 +477,7 @@ GptqLayout gptq_layout(int64_t N, int64_t K) {
   const size_t npad = (size_t)((N + 63) / 64) * 64;
   L.m = take(sizeof(double) * K * K);
   L.y = take(sizeof(double) * K * K);
+  L.tmp = take(sizeof(double) * K * K / 4);
   L.w64 = take(sizeof(double) * N * K);
   L.et = take(sizeof(double) * kColBlock * npad);
   L.dead = take((size_t)K);
@@ -415,7 +493,7 @@ hipError_t run_columns(const double* U, double* W64, double* Et, int64_t N, int6
     if (G >= kColBlock && c0 % G == 0)
       hipLaunchKernelGGL((wide_group_params_kernel<BITS, ASYM>), dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream,
                          W64, N, K, G, c0, scales, zeros);
-    hipLaunchKernelGGL((gptq_block_kernel<BITS, ASYM>), dim3((unsigned)(npad / 64)), dim3(64), 0, stream, W64, U, N, K,
+    hipLaunchKernelGGL((gptq_block_kernel<BITS, ASYM>), dim3((unsigned)(npad / 64)), dim3(64 * kBlockWaves), 0, stream, W64, U, N, K,
                        G, c0, npad, packed, scales, zeros, Et);
     if (c0 + kColBlock < K)
       hipLaunchKernelGGL(gptq_update_kernel, dim3((unsigned)(npad / 64), (unsigned)((K - c0 - kColBlock) / 64)),
@@ -440,6 +518,7 @@ hipError_t launch_gptq(const void* X, const void* W, int64_t T, int64_t N, int64
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   double* M = reinterpret_cast<double*>(ws + L.m);
   double* Y = reinterpret_cast<double*>(ws + L.y);
+  double* Tmp = reinterpret_cast<double*>(ws + L.tmp);
   double* W64 = reinterpret_cast<double*>(ws + L.w64);
   double* Et = reinterpret_cast<double*>(ws + L.et);
   uint8_t* dead = ws + L.dead;
@@ -449,20 +528,23 @@ hipError_t launch_gptq(const void* X, const void* W, int64_t T, int64_t N, int64
   hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(256), 0, stream, M, K, damp, dead);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const unsigned fill_blocks = 2048;
+  hipLaunchKernelGGL(zero_kernel, dim3(fill_blocks), dim3(256), 0, stream, Y, K * K);
   for (int p = 0; p < nb; ++p) {
-    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, stream, M, K, p);
+    hipLaunchKernelGGL(potrf_inv_kernel, dim3(1), dim3(64), 0, stream, M, Y, K, p);
     const int m = nb - 1 - p;
     if (m > 0) {
-      hipLaunchKernelGGL(trsm_panel_kernel, dim3(m), dim3(64), 0, stream, M, K, p);
+      hipLaunchKernelGGL(trsm_panel_kernel, dim3(m), dim3(256), 0, stream, M, Y, K, p);
       hipLaunchKernelGGL(syrk_trailing_kernel, dim3(m, m), dim3(256), 0, stream, M, K, p);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  for (int i = 0; i < nb; ++i) {
-    hipLaunchKernelGGL(trtri_row_kernel, dim3(i + 1), dim3(256), 0, stream, M, Y, K, i);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int64_t s = kPanel; s < K; s *= 2) {
+    const unsigned t = (unsigned)(s / 64), pairs = (unsigned)((K + 2 * s - 1) / (2 * s));
+    hipLaunchKernelGGL(pair_left_kernel, dim3(t, t, pairs), dim3(256), 0, stream, M, Y, K, s, Tmp);
+    hipLaunchKernelGGL(pair_right_kernel, dim3(t, t, pairs), dim3(256), 0, stream, Y, K, s, Tmp);
   }
-  const unsigned fill_blocks = 2048;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(reverse_factor_kernel, dim3(fill_blocks), dim3(256), 0, stream, Y, K, M);
   hipLaunchKernelGGL(init_weights_kernel, dim3(fill_blocks), dim3(256), 0, stream, static_cast<const uint16_t*>(W),
                      dead, N, K, W64);

@@ -17,9 +17,11 @@ GPU idle time inside the events.  The CPU oracle is timed on a bounded sample
 of the same workload (cpu_baseline).
 
 The same run also times the other rows of the path on their own workloads
-(`rows`): the LLaMA-2-7B-shaped decode GEMVs with AWQ scales, the small-batch
+(`rows`): the LLaMA-2-7B-shaped decode GEMVs with AWQ scales, the fused
+projection GEMVs, the group sizes 32 / 64 / 128 / K, the small-batch
 GEMM (M = 4, 16, 64; K = 8192, N = 28672), the prefill GEMM (M = 2048,
-K = 4096, N = 11008) and quantize_pack over 32 layers of the LLaMA-2-7B linear
+K = 4096, N = 11008), the AWQ exponent search and GPTQ for the q_proj shape,
+and quantize_pack over 32 layers of the LLaMA-2-7B linear
 shapes, each as back-to-back launches over rotated weight sets with its
 roofline fraction and a sampled check against the oracle.
 
@@ -45,6 +47,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA (no sparsity)
+FP64_PEAK_TFLOPS = 78.6        # MI355X fp64 (vector and matrix)
 MALL_BYTES = 256 << 20
 METRIC = "W4A16 g128 GEMV µs + effective HBM GB/s (% peak) at M=1, K=N=8192"
 GEMV_BURST = 8
@@ -358,7 +361,12 @@ def time_rows(torch, ops, synth):
         return float(((Xg.float() @ D.T).double() ** 2).sum())
 
     lg, lr = layer_loss(ops.gptq(Xg, Wg, 4, 128, True)), layer_loss(ops.quantize_pack(Wg, 4, 128, True))
-    rows["gptq_q_proj"] = {"T": T, "N": N, "K": K, "ms": round(us / 1e3, 3),
+    # algorithmic fp64 flops: lower triangle of 2 X^T X, Cholesky, triangular
+    # inverse, and the error propagation into later columns
+    flop = T * K * (K + 1) + K ** 3 / 3 + K ** 3 / 3 + N * K * K
+    rows["gptq_q_proj"] = {"T": T, "N": N, "K": K, "ms": round(us / 1e3, 3), "fp64_flop": flop,
+                           "tflops": round(flop / us / 1e6, 2),
+                           "frac_fp64": round(flop / us / 1e6 / FP64_PEAK_TFLOPS, 4),
                            "loss_gptq_over_rtn": float(f"{lg / lr:.4g}")}
     del Xg, Wg
 

@@ -386,6 +386,20 @@ def test_gemm_large_m_tiles(xdtype, bits, asym, G, K, awq):
     gemm_case(W, X, xdtype, bits, asym, G=G, s=s, label="large-M")
 
 
+@pytest.mark.parametrize("asym,awq", [(True, False), (False, True)])
+def test_gemm_large_m_full_chip_f16(asym, awq):
+    # fp16, 4-bit: a 4096 x 4096 output is 256 tiles of 256 x 256, one round
+    # of compute units, which the LDS-staged kernel takes; smaller or ragged
+    # tile counts go to the register-B kernel (the other large-M tests).
+    rng = np.random.default_rng(41 + int(asym))
+    M, N, K = 4096, 4096, 256
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    s = np.exp(rng.uniform(-1.0, 1.0, K)).astype(np.float32) if awq else None
+    rows = np.concatenate([np.sort(rng.choice(N, 64, replace=False)), [N - 1]])
+    gemm_case(W, X, "f16", 4, asym, s=s, rows=rows, label="full-chip")
+
+
 def test_gemm_large_m_one_hot_rows_f16():
     # fp16 large-M path: w_hat is rounded once to fp16, so a one-hot row of X
     # returns that rounding bit for bit.

@@ -464,9 +464,20 @@ hipError_t launch_asym(const void* X, int xdtype, const float* s, const void* pa
 // kernel; its fp16 variant steps K by 64.
 constexpr int64_t kLdsGemmMinM = 128;
 
+// The LDS-staged kernel's 256 x 256 tiles do more per tile than the
+// register-B kernel's 128 x 256 tiles, but only pay off when they fill the
+// 256 compute units in whole rounds (at least 95% of the last round busy).
+static bool lds_tiles_fill_chip(int64_t M, int64_t N) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t rounds = (tiles + 255) / 256;
+  return tiles * 100 >= rounds * 256 * 95;
+}
+
 hipError_t launch_gemm(const void* X, int xdtype, const float* act_scale, const void* packed, const void* scales,
                        const void* zeros, int64_t M, int64_t N, int64_t K, int bits, int group_size, bool asymmetric,
                        void* Y, hipStream_t stream) {
+  if (M >= kLdsGemmMinM && xdtype == 0 && bits == 4 && K % 64 == 0 && !lds_tiles_fill_chip(M, N))
+    return launch_gemm_regb(X, act_scale, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, stream);
   if (M >= kLdsGemmMinM && (xdtype != 0 || K % 64 == 0))
     return launch_gemm_lds(X, xdtype, act_scale, packed, scales, zeros, M, N, K, bits, group_size, asymmetric, Y,
                            stream);

@@ -1,0 +1,321 @@
+// Large-M fused dequantize + GEMM with the weights decoded straight into
+// matrix-core operand registers (fp16 activations, 4-bit codes).
+//
+// At large M the product is compute-bound ("CMU 11-868 L19-L20", section
+// "Back to the question: where does the speed come from?"), so the weights
+// only have to be dequantized once per use in a tile and fed to fp16 MFMA.
+// This kernel spends LDS only on the activations:
+//
+//   * A workgroup of 4 waves computes a 128 x 256 tile of Y; wave w owns
+//     columns [64 w, 64 w + 64) for all 128 rows (4 x 2 tiles of
+//     v_mfma_f32_32x32x16_f16, 128 fp32 accumulators per lane), so no weight
+//     is decoded twice.
+//   * X[m0:m0+128, k:k+64] goes through a double-buffered LDS stage (one
+//     barrier per 64-wide K block) and is read back as A fragments.
+//   * B fragments never touch LDS.  Inside one 64-wide K block, lane half h of
+//     a wave supplies K offsets [32 h, 32 h + 32) over the four 16-deep MFMA
+//     steps (step s: offsets 32 h + 8 s .. + 8) instead of the usual 8 h + 16 s
+//     ordering; A fragments are read with the same mapping, so each step still
+//     sums every K offset exactly once.  With that order a lane's B data for
+//     the whole block is one 16-byte chunk of layout v1 (32 codes of one
+//     output column, inside one group since G % 32 == 0), and the code word s
+//     of the chunk holds exactly the 8 K offsets of step s, as the pairs
+//     (w >> 4t) & 0x000F000F, t = 0..3.
+//   * Each pair is widened exactly, (1024 + u) - (1024 + Z) = u - Z in fp16,
+//     and multiplied by S once: the weight is the same fp16 w_hat as in the
+//     LDS-staged kernel.  With an AWQ scale, A holds x * fl32(1 / s) rounded
+//     once to fp16, also as there.
+//
+// The tile's scales and zero points (K / G <= 40 groups) are staged in LDS
+// once, with contiguous loads: one 2-byte load per lane and block from 32
+// different rows would cost as much as the codes themselves.  Loads for
+// block k + 1 (X into registers and the codes) are issued at the top of block
+// k, before block k's codes are first used, so they stay in flight through
+// block k's MFMAs.  Tiles are assigned so
+// that each of the 8 XCDs works on a contiguous range of the tile grid with
+// the N tile index fastest.
+//
+// MFMA operand slots (32x32x16): lane l supplies A[m = l%32][8(l/32)+j] and
+// B[8(l/32)+j][n = l%32] (j = 0..7, here K offsets 32(l/32) + 8s + j) and
+// holds C[m = 8(v/4) + 4(l/32) + v%4][n = l%32] in accumulator v = 0..15.
+#include "woq_device.h"
+#include "woq_internal.h"
+
+namespace woq {
+namespace {
+
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kBM = 128, kBN = 256, kBK = 64;
+constexpr int kThreads = 256;
+constexpr int kLD = kBK + 8;                          // A row pitch in halves (144 B: conflict-free ds_read_b128)
+constexpr int kStage = kBM * kLD;                     // halves per A stage
+constexpr int kASegs = kBK / 8;                       // 16-byte segments per A row
+constexpr int kAUnits = kBM * kASegs / kThreads;      // A segments per thread
+constexpr int kARowStep = kThreads / kASegs;          // rows between a thread's segments
+constexpr int kSZMaxGroups = 40;                      // K / G up to which S and Z are staged in LDS
+constexpr int kSZWords = kBN * (kSZMaxGroups + 1);    // S | Z << 16 per (column, group), odd pitch
+
+__device__ inline float16_t mfma32(u32x4_t a, u32x4_t b, float16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0,
+                                                0, 0);
+}
+
+// fp16 pair (u - Z) * S from the pair 1024 + u (codes OR-ed into 0x6400).
+__device__ inline uint32_t dequant_pair(uint32_t magic_codes2, uint32_t zmagic2, uint32_t s2) {
+  const h2_t p = __builtin_bit_cast(h2_t, magic_codes2);
+  const h2_t d = p - __builtin_bit_cast(h2_t, zmagic2);
+  return __builtin_bit_cast(uint32_t, d * __builtin_bit_cast(h2_t, s2));
+}
+
+template <bool ASYM, bool SCALE, bool SZL>
+__global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
+    const uint16_t* __restrict__ X, const float* __restrict__ s, const uint8_t* __restrict__ packed,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int M, int N, int K, int G,
+    uint16_t* __restrict__ Y, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+  __shared__ uint32_t szs[SZL ? kSZWords : 1];
+
+  const int T = tiles_m * tiles_n;
+  const int per_xcd = (T + 7) / 8;
+  const int tile = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (tile >= T) return;
+  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+  const int m0 = tm * kBM, n0 = tn * kBN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 31, fh = lane >> 5;
+  const int gpr = K / G;
+  const int kblocks = K / kBK;
+
+  // A staging: thread t owns segment t % 8 of rows t / 8 + 32 i.  Rows past M
+  // read row M - 1; their outputs are never stored.
+  const int a_seg = tid % kASegs, a_r0 = tid / kASegs;
+  const uint16_t* a_src[kAUnits];
+#pragma unroll
+  for (int i = 0; i < kAUnits; ++i) {
+    const int r = m0 + a_r0 + kARowStep * i;
+    a_src[i] = X + (int64_t)(r < M ? r : M - 1) * K + 8 * a_seg;
+  }
+  const uint32_t a_dst = (uint32_t)(a_r0 * kLD + 8 * a_seg);
+
+  // B: subtile j of this wave is column n0 + 64 wave + 32 j + l%32 (columns
+  // past N read column N - 1, never stored); this lane's chunk of a block
+  // starting at k is codes [k + 32 h, k + 32 h + 32).
+  const uint8_t* b_src[2];
+  int64_t g_row[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int c = n0 + 64 * wave + 32 * j + fr;
+    c = c < N ? c : N - 1;
+    b_src[j] = packed + (int64_t)c * (K / 2) + 16 * fh;
+    g_row[j] = (int64_t)c * gpr;
+  }
+
+  // SZL: the tile's scales and zero points, S | Z << 16 per (column, group)
+  // with pitch gpr + 1 (conflict-free for 32 consecutive columns), loaded
+  // once with contiguous 2-byte loads; otherwise every block loads its own.
+  const int szp = gpr + 1;
+  if constexpr (SZL) {
+    const int total = kBN * gpr, q = kThreads / gpr, r = kThreads % gpr;
+    int c = tid / gpr, g = tid % gpr;
+    const int64_t row0 = (int64_t)n0 * gpr;
+    const int64_t limit = (int64_t)N * gpr;
+    for (int idx = tid; idx < total; idx += kThreads) {
+      int64_t gi = row0 + idx;
+      gi = gi < limit ? gi : limit - 1;  // columns past N: any valid value (never stored)
+      const uint32_t sv = scales[gi], zv = ASYM ? zeros[gi] : 0u;
+      szs[c * szp + g] = sv | (zv << 16);
+      c += q;
+      g += r;
+      if (g >= gpr) {
+        g -= gpr;
+        ++c;
+      }
+    }
+  }
+
+  struct ARegs {
+    u32x4_t a[kAUnits];
+  };
+  struct BRegs {
+    u32x4_t w[2];
+    uint16_t s16[2], z16[2];
+  };
+  auto load_a = [&](ARegs& R, int kb) {
+#pragma unroll
+    for (int i = 0; i < kAUnits; ++i) R.a[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + kb);
+  };
+  auto load_b = [&](BRegs& R, int kb) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      R.w[j] = *reinterpret_cast<const u32x4_t*>(b_src[j] + kb / 2);
+      if constexpr (!SZL) {
+        const int64_t gi = g_row[j] + (kb + 32 * fh) / G;
+        R.s16[j] = scales[gi];
+        R.z16[j] = ASYM ? zeros[gi] : (uint16_t)0;
+      }
+    }
+  };
+  auto store_a = [&](const ARegs& R, int st, int kb) {
+    uint16_t* base = lds + st * kStage;
+    float inv[8];
+    if constexpr (SCALE) {
+      const float4_t s0 = *reinterpret_cast<const float4_t*>(s + kb + 8 * a_seg);
+      const float4_t s1 = *reinterpret_cast<const float4_t*>(s + kb + 8 * a_seg + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        inv[e] = 1.0f / s0[e];
+        inv[e + 4] = 1.0f / s1[e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kAUnits; ++i) {
+      u32x4_t v = R.a[i];
+      if constexpr (SCALE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = F16::to_f32((uint16_t)(v[e] & 0xFFFFu)) * inv[2 * e];
+          const float x1 = F16::to_f32((uint16_t)(v[e] >> 16)) * inv[2 * e + 1];
+          v[e] = (uint32_t)F16::from_f32(x0) | ((uint32_t)F16::from_f32(x1) << 16);
+        }
+      }
+      *reinterpret_cast<u32x4_t*>(base + a_dst + kARowStep * kLD * i) = v;
+    }
+  };
+
+  float16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const uint32_t a_rd = (uint32_t)(fr * kLD + 32 * fh);
+  const uint32_t magic = vgpr_const(0x64006400u);  // one v_and_or_b32 per pair
+  const float zsym = 8.0f;
+  auto mma_block = [&](int st, const BRegs& R, int kb) {
+    const uint16_t* base = lds + st * kStage;
+    uint32_t zm[2], s2[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint16_t s16, z16;
+      if constexpr (SZL) {
+        const uint32_t v = szs[(64 * wave + 32 * j + fr) * szp + (kb + 32 * fh) / G];
+        s16 = (uint16_t)(v & 0xFFFFu);
+        z16 = (uint16_t)(v >> 16);
+      } else {
+        s16 = R.s16[j];
+        z16 = R.z16[j];
+      }
+      const float Z = ASYM ? half_bits_to_f32(z16) : zsym;
+      const uint32_t zh = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(1024.0f + Z));
+      zm[j] = zh | (zh << 16);
+      s2[j] = (uint32_t)s16 | ((uint32_t)s16 << 16);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4_t a[4], b[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4_t*>(base + a_rd + 32 * kLD * i + 8 * ks);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t w = R.w[j][ks];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) b[j][t] = dequant_pair(((w >> (4 * t)) & 0x000F000Fu) | magic, zm[j], s2[j]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    }
+  };
+
+  // Block kt: loads for block kt + 1 first (clamped to the last block at the
+  // end: reloads never used), then block kt's MFMAs with its codes, then X of
+  // block kt + 1 into the other LDS stage; one barrier per block.
+  const int last = kblocks - 1;
+  ARegs RA;
+  BRegs RB, RN;
+  load_a(RA, 0);
+  load_b(RB, 0);
+  store_a(RA, 0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < kblocks; ++kt) {
+    const int nxt = kt + 1 < kblocks ? kt + 1 : last;
+    load_a(RA, nxt * kBK);
+    load_b(RN, nxt * kBK);
+    // keep the loads ahead of the MFMAs (the scheduler would otherwise sink
+    // them next to their first use)
+    __builtin_amdgcn_sched_barrier(0);
+    mma_block(kt & 1, RB, kt * kBK);
+    store_a(RA, (kt + 1) & 1, nxt * kBK);
+    RB = RN;
+    __syncthreads();
+  }
+
+  // Epilogue: for accumulator (i, j, v) the 32 lanes of each half-wave hold
+  // 32 consecutive columns of one row.
+  const int row_base = m0 + 4 * fh;
+  const int col_base = n0 + 64 * wave + fr;
+  uint16_t* __restrict__ yb = Y + (int64_t)row_base * N + col_base;
+  if (m0 + kBM <= M && n0 + kBN <= N) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        uint16_t* __restrict__ yr = yb + (int64_t)(32 * i + 8 * (v >> 2) + (v & 3)) * N;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) yr[32 * j] = F16::from_f32(acc[i][j][v]);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int dm = 32 * i + 8 * (v >> 2) + (v & 3);
+        if (row_base + dm >= M) continue;
+        uint16_t* __restrict__ yr = yb + (int64_t)dm * N;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (col_base + 32 * j < N) yr[32 * j] = F16::from_f32(acc[i][j][v]);
+      }
+  }
+}
+
+template <bool ASYM, bool SCALE, bool SZL>
+hipError_t launch_sz(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
+                     int64_t M, int64_t N, int64_t K, int G, void* Y, hipStream_t stream) {
+  const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
+  const int T = tiles_m * tiles_n;
+  const unsigned blocks = 8u * (unsigned)((T + 7) / 8);
+  hipLaunchKernelGGL((gemm_regb_kernel<ASYM, SCALE, SZL>), dim3(blocks), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
+                     static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N, (int)K,
+                     G, static_cast<uint16_t*>(Y), tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <bool ASYM, bool SCALE>
+hipError_t launch_one(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
+                      int64_t M, int64_t N, int64_t K, int G, void* Y, hipStream_t stream) {
+  return K / G <= kSZMaxGroups ? launch_sz<ASYM, SCALE, true>(X, s, packed, scales, zeros, M, N, K, G, Y, stream)
+                               : launch_sz<ASYM, SCALE, false>(X, s, packed, scales, zeros, M, N, K, G, Y, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_regb(const void* X, const float* act_scale, const void* packed, const void* scales,
+                            const void* zeros, int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric,
+                            void* Y, hipStream_t stream) {
+  if (asymmetric)
+    return act_scale ? launch_one<true, true>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream)
+                     : launch_one<true, false>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream);
+  return act_scale ? launch_one<false, true>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream)
+                   : launch_one<false, false>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream);
+}
+
+}  // namespace woq

@@ -29,6 +29,12 @@ hipError_t launch_gemm_lds(const void* X, int xdtype, const float* act_scale, co
                            const void* scales, const void* zeros, int64_t M, int64_t N, int64_t K, int bits,
                            int group_size, bool asymmetric, void* Y, hipStream_t stream);
 
+// Large-M GEMM for fp16 activations and 4-bit codes (K % 64 == 0): 128 x 256
+// tiles, weights decoded straight into MFMA operand registers.
+hipError_t launch_gemm_regb(const void* X, const float* act_scale, const void* packed, const void* scales,
+                            const void* zeros, int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric,
+                            void* Y, hipStream_t stream);
+
 // AWQ exponent search (scratch in the caller's workspace).
 size_t awq_search_workspace_bytes(int64_t T, int64_t N, int64_t K, int bits, int group_size, bool asymmetric);
 hipError_t launch_awq_search(const void* X, const void* W, int64_t T, int64_t N, int64_t K, int bits,
@@ -36,8 +42,8 @@ hipError_t launch_awq_search(const void* X, const void* W, int64_t T, int64_t N,
                              int32_t* best_index, void* workspace, hipStream_t stream);
 
 // Y[m, n] = sum_k A[m, k] B[n, k] in fp32 for fp16 A [M, K], B [N, K]
-// (K % 16 == 0): the dense MFMA product the AWQ and GPTQ passes use for
-// reference outputs and Hessians.
+// (K % 16 == 0): the dense MFMA product the AWQ search uses for its
+// reference output.
 hipError_t launch_dense_ref(const void* A, const void* B, int64_t M, int64_t N, int64_t K, float* Y,
                             hipStream_t stream);
 

@@ -133,11 +133,13 @@ woq_status woq_w4a16_gemv(const void* x, int32_t xdtype, const float* act_scale,
 /* Y[m, n] = sum_k (X[m, k] / s[k]) * w_hat[n, k]  for M >= 1.
  *   X : [M, K] row-major of xdtype;  Y : out, [M, N] row-major of xdtype.
  * Small M decodes weights in registers and feeds MFMA with an exact integer
- * (u - Z) and per-group fp32 scaling; large M (M >= 128 and, for fp16,
- * K % 64 == 0) stages dequantized tiles in LDS for MFMA: w_hat rounded once to
- * fp16 with X * fl32(1 / s) rounded once to fp16, or, for bf16, X used as
- * given and w_hat * fl32(1 / s) kept as a bf16 pair hi + lo (about 16
- * significant bits).  fp32 accumulation throughout. */
+ * (u - Z) and per-group fp32 scaling.  Large M (M >= 128 and, for fp16,
+ * K % 64 == 0) feeds MFMA with dequantized weights: for fp16, w_hat rounded
+ * once to fp16 (decoded straight into operand registers for 4-bit codes, or
+ * staged in LDS) with X * fl32(1 / s) rounded once to fp16; for bf16, X used
+ * as given and w_hat * fl32(1 / s) kept as a bf16 pair hi + lo (about 16
+ * significant bits).  fp32 accumulation throughout; the order of the K sum
+ * inside an MFMA step is the kernel's. */
 woq_status woq_w4a16_gemm(const void* X, int32_t xdtype, const float* act_scale,
                           const void* packed, const void* scales, const void* zeros,
                           int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size,

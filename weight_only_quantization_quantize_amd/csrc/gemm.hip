@@ -460,8 +460,9 @@ hipError_t launch_asym(const void* X, int xdtype, const float* s, const void* pa
 
 }  // namespace
 
-// Rows of X from which the LDS-staged MFMA kernel replaces the direct-decode
-// kernel; its fp16 variant steps K by 64.
+// Rows of X from which the large-M kernels (gemm_regb.hip for fp16 with
+// 4-bit codes, gemm_lds.hip otherwise) replace the direct-decode kernel; both
+// step K by 64 for fp16.
 constexpr int64_t kLdsGemmMinM = 128;
 
 // The LDS-staged kernel's 256 x 256 tiles do more per tile than the

@@ -1,4 +1,7 @@
-// Large-M fused dequantize + GEMM on gfx950 matrix cores (prefill shapes).
+// Large-M fused dequantize + GEMM on gfx950 matrix cores (prefill shapes):
+// bf16 activations, 3-bit codes, and fp16 shapes whose 256 x 256 tiles fill
+// the compute units in whole rounds (fp16 with 4-bit codes otherwise goes to
+// gemm_regb.hip).
 //
 // At large M the product is compute-bound, which is why weight-only
 // quantization brings no speed-up there ("CMU 11-868 L19-L20", section "Back

@@ -24,7 +24,8 @@ hipError_t launch_gemm(const void* X, int xdtype, const float* act_scale, const 
                        const void* scales, const void* zeros, int64_t M, int64_t N, int64_t K, int bits,
                        int group_size, bool asymmetric, void* Y, hipStream_t stream);
 
-// Large-M GEMM: LDS-staged 256 x 256 tiles on 32x32x16 MFMA.
+// Large-M GEMM: LDS-staged 256 x 256 tiles on 32x32x16 MFMA (bf16, 3-bit,
+// and fp16 shapes whose tiles fill the chip).
 hipError_t launch_gemm_lds(const void* X, int xdtype, const float* act_scale, const void* packed,
                            const void* scales, const void* zeros, int64_t M, int64_t N, int64_t K, int bits,
                            int group_size, bool asymmetric, void* Y, hipStream_t stream);

@@ -465,7 +465,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is not sharded "
-              "across GPUs in this build)", file=sys.stderr)
+              "across GPUs by this library)", file=sys.stderr)
         sys.exit(2)
 
     if args.write_traffic:

@@ -24,7 +24,8 @@
 // subnormals of value u * 2^-24 (resp. 16u * 2^-24), which v_dot2 multiplies
 // exactly; one AND per pair and
 //   sum x (u - Z) = 2^24 (a + b / 16) - Z * sum x.
-// 3-bit pairs are reassembled in the low bits the same way.  bf16 activations
+// 3-bit codes are dotted in two parts, u = lo + 4 hi, each masked where it
+// sits (partial sums of known power-of-two weight) instead of reassembled.  bf16 activations
 // OR the pair into the 16-bit float MAGIC + u (0x4300 = 128) and remove
 // (MAGIC + Z) * sum x instead.
 //
@@ -112,9 +113,30 @@ __device__ inline float chunk_dot(const Codes<BITS>& c, const uint32_t (&xr)[16]
       for (int t = 0; t < 4; ++t) a = XT::dot2(((c.w[j] >> (4 * t)) & 0x000F000Fu) | magic, xr[4 * j + t], a);
     return a - (XT::kMagic + Z) * (xs.part[0] + xs.part[1]);
   } else if constexpr (kF16) {
-    float a = 0.0f;
+    // u = lo + 4 hi, each part dotted where it sits in its word, as fp16
+    // subnormals of a known power-of-two weight (one AND and one dot2 per
+    // masked pair, no bit moves): the low pairs t = 2q, 2q + 1 of word
+    // w_(t/8) are (w >> 4q) & 0x00030003 (weight 1) and & 0x000C000C
+    // (weight 4); the high bit of pair t = 4q + j is (w2 >> 4q) & (0x00010001
+    // << j) (weight 2^j).
+    float l0 = 0.0f, l1 = 0.0f, h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int t = 0; t < 16; ++t) a = XT::dot2(pair3(c.w0, c.w1, c.w2, t, 0u), xr[t], a);
+    for (int wi = 0; wi < 2; ++wi) {
+      const uint32_t w = wi ? c.w1 : c.w0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t ws = w >> (4 * q);
+        l0 = XT::dot2(ws & 0x00030003u, xr[8 * wi + 2 * q], l0);
+        l1 = XT::dot2(ws & 0x000C000Cu, xr[8 * wi + 2 * q + 1], l1);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t ws = c.w2 >> (4 * q);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h[j] = XT::dot2(ws & (0x00010001u << j), xr[4 * q + j], h[j]);
+    }
+    const float a = l0 + 0.25f * l1 + 4.0f * h[0] + 2.0f * h[1] + h[2] + 0.5f * h[3];
     return 16777216.0f * a - Z * (xs.part[0] + xs.part[1]);
   } else {
     float a = 0.0f;

@@ -51,7 +51,7 @@ woq_status check_qparams(int64_t N, int64_t K, int32_t bits, int32_t group_size)
     return fail(WOQ_ERR_INVALID_ARGUMENT, "K (%lld) must be a multiple of group_size (%d)", (long long)K,
                 group_size);
   if (N > INT32_MAX || K > INT32_MAX / 2)
-    return fail(WOQ_ERR_UNSUPPORTED, "N or K too large for this build (N=%lld, K=%lld)", (long long)N,
+    return fail(WOQ_ERR_UNSUPPORTED, "N or K too large for this library (N=%lld, K=%lld)", (long long)N,
                 (long long)K);
   return WOQ_OK;
 }
@@ -102,7 +102,7 @@ woq_status check_gptq(int64_t T, int64_t N, int64_t K, int32_t bits, int32_t gro
   if (128 % group_size != 0 && group_size % 128 != 0)
     return fail(WOQ_ERR_UNSUPPORTED, "gptq needs group_size dividing 128 or a multiple of 128 (got %d)", group_size);
   if (K > 32768 || T > INT32_MAX || N > ((int64_t)1 << 31))
-    return fail(WOQ_ERR_UNSUPPORTED, "gptq sizes too large for this build (T=%lld, N=%lld, K=%lld)", (long long)T,
+    return fail(WOQ_ERR_UNSUPPORTED, "gptq sizes too large for this library (T=%lld, N=%lld, K=%lld)", (long long)T,
                 (long long)N, (long long)K);
   return WOQ_OK;
 }
@@ -182,7 +182,7 @@ woq_status woq_w4a16_gemm(const void* X, int32_t xdtype, const float* act_scale,
   (void)workspace_bytes;
   WOQ_TRY(check_qparams(N, K, bits, group_size));
   if (M < 1) return fail(WOQ_ERR_INVALID_ARGUMENT, "M must be >= 1 (got %lld)", (long long)M);
-  if (M > INT32_MAX / 2) return fail(WOQ_ERR_UNSUPPORTED, "M too large for this build (%lld)", (long long)M);
+  if (M > INT32_MAX / 2) return fail(WOQ_ERR_UNSUPPORTED, "M too large for this library (%lld)", (long long)M);
   if (xdtype != WOQ_F16 && xdtype != WOQ_BF16)
     return fail(WOQ_ERR_INVALID_ARGUMENT, "xdtype must be WOQ_F16 or WOQ_BF16 (got %d)", xdtype);
   if (!X || !Y) return fail(WOQ_ERR_INVALID_ARGUMENT, "X and Y must not be NULL");
@@ -227,7 +227,7 @@ woq_status woq_awq_search(const void* X, const void* W, int64_t T, int64_t N, in
   WOQ_TRY(check_qparams(N, K, bits, group_size));
   if (T < 1) return fail(WOQ_ERR_INVALID_ARGUMENT, "T must be >= 1 (got %lld)", (long long)T);
   if (T > INT32_MAX / 2 || T * N > (int64_t)1 << 40)
-    return fail(WOQ_ERR_UNSUPPORTED, "T x N too large for this build (T=%lld, N=%lld)", (long long)T, (long long)N);
+    return fail(WOQ_ERR_UNSUPPORTED, "T x N too large for this library (T=%lld, N=%lld)", (long long)T, (long long)N);
   if (n_grid < 1 || n_grid > 64) return fail(WOQ_ERR_INVALID_ARGUMENT, "n_grid must be in [1, 64] (got %d)", n_grid);
   if (!X || !W) return fail(WOQ_ERR_INVALID_ARGUMENT, "X and W must not be NULL");
   if (!aligned(X, 16) || !aligned(W, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "X and W must be 16-byte aligned");

@@ -383,6 +383,7 @@ __global__ __launch_bounds__(64 * kBlockWaves) void gptq_block_kernel(
     p.S = half_bits_to_f32(p.S16);
     p.Z = ASYM ? (int)half_bits_to_f32(zeros[gi]) : 1 << (BITS - 1);
     p.zero = p.S == 0.0f;
+    set_reciprocal(p);
   }
   for (int c = 0; c < kColBlock; ++c) {
     const int owner = c / kOwn, slot = c % kOwn;

@@ -1,8 +1,8 @@
 // Round-to-nearest rules shared by every kernel that decides codes: the
 // group scale / zero point and the code of one weight, each decision one
-// correctly rounded binary32 operation (IEEE division, rintf = round half to
-// even, fp32 -> fp16 round-to-nearest-even with subnormals), and the layout-v1
-// store of a 32-code chunk.
+// correctly rounded binary32 operation (IEEE division or its exact
+// equivalent, rintf = round half to even, fp32 -> fp16 round-to-nearest-even
+// with subnormals), and the layout-v1 store of a 32-code chunk.
 //
 //   symmetric : S = f16(max|w| / (2^(b-1)-1)), u = clip(rne(w/S), -2^(b-1), 2^(b-1)-1) + 2^(b-1)
 //   asymmetric: r = max-min (1 if 0), S = f16(r / (2^b-1)),
@@ -27,10 +27,29 @@ __device__ inline uint16_t f32_to_half_bits(float f) { return __builtin_bit_cast
 template <int BITS, bool ASYM>
 struct GroupParams {
   float S;        // the stored fp16 scale, widened exactly
+  float R;        // fl32(1 / S), IEEE division (0 when S == 0)
   int Z;          // zero point (symmetric: 2^(b-1))
   uint16_t S16;   // fp16 bits of S
   bool zero;      // S == 0: every code is Z
 };
+
+// fl32(w / S) from R = fl32(1 / S) without a division: q0 = w R is within
+// about one ulp of w / S, each residual w - q S is exact in an fma, and two
+// correction steps give the correctly rounded quotient (Markstein's
+// division with a correctly rounded reciprocal).  Checked on the GPU against
+// IEEE division for every finite fp16 w and positive fp16 S, and for 2^34
+// random fp32 w: equal everywhere except the sign of a zero quotient, which
+// the rounding to an integer code ignores.
+__device__ inline float div_by_scale(float w, float S, float R) {
+  const float q0 = w * R;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, S, w), R, q0);
+  return __builtin_fmaf(__builtin_fmaf(-q1, S, w), R, q1);
+}
+
+template <int BITS, bool ASYM>
+__device__ inline void set_reciprocal(GroupParams<BITS, ASYM>& p) {
+  p.R = p.zero ? 0.0f : 1.0f / p.S;
+}
 
 template <int BITS, bool ASYM>
 __device__ inline GroupParams<BITS, ASYM> group_params(float lo, float hi) {
@@ -55,6 +74,7 @@ __device__ inline GroupParams<BITS, ASYM> group_params(float lo, float hi) {
       p.Z = z < 0 ? 0 : (z > (1 << BITS) - 1 ? (1 << BITS) - 1 : z);
     }
   }
+  set_reciprocal(p);
   return p;
 }
 
@@ -62,7 +82,7 @@ __device__ inline GroupParams<BITS, ASYM> group_params(float lo, float hi) {
 template <int BITS, bool ASYM>
 __device__ inline uint32_t code_of(float w, const GroupParams<BITS, ASYM>& p) {
   if (p.zero) return (uint32_t)p.Z;
-  int q = (int)__builtin_rintf(w / p.S);
+  int q = (int)__builtin_rintf(div_by_scale(w, p.S, p.R));
   if (!ASYM) {
     const int h = 1 << (BITS - 1);
     q = q < -h ? -h : (q > h - 1 ? h - 1 : q);

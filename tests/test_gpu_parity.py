@@ -137,6 +137,32 @@ def test_quantize_pack_adversarial_groups(bits, asym):
     assert_pack_equal(gpu, ref)
 
 
+def _every_fp16_weight_groups(m_bits):
+    """Groups of 128 fp16 weights whose largest magnitude is the fp16 value
+    with bits m_bits (so every group has the same scale) and whose other 127
+    weights run through every finite fp16 value of magnitude <= m, both
+    signs: each code decision w / S of the quantizer is exercised for every
+    such w at that S."""
+    m = np.array([m_bits], np.uint16).view(np.float16)[0]
+    allv = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    vals = allv[np.isfinite(allv) & (np.abs(allv.astype(np.float32)) <= np.float32(m))]
+    n = -(-len(vals) // 127)
+    body = np.resize(vals, n * 127).reshape(n, 127)
+    return np.concatenate([np.full((n, 1), m, np.float16), body], axis=1)
+
+
+@pytest.mark.parametrize("bits,asym", [(4, False), (4, True), (3, False)])
+def test_quantize_pack_every_fp16_weight_at_sampled_scales(bits, asym):
+    # The kernels compute w / S from the group's reciprocal with exact fma
+    # corrections; the oracle divides.  Every finite fp16 weight against the
+    # scales of 12 group maxima spread over the fp16 range (subnormal to 2^15).
+    maxima = [0x0001, 0x0155, 0x03FF, 0x0400, 0x1A3B, 0x2E66, 0x3555, 0x3C00, 0x4248, 0x5A5A, 0x6BCD, 0x7BFF]
+    W = np.concatenate([_every_fp16_weight_groups(mb) for mb in maxima], axis=0)  # one group per row
+    _say(f"quantize_pack every fp16 weight: {W.shape} bits={bits} asym={asym}")
+    gpu, ref = quantize_both(W, bits, 128, asym)
+    assert_pack_equal(gpu, ref)
+
+
 def test_quantize_pack_worked_example():
     # "LLM Quantization: 160GB Model on a Laptop", section "Symmetric
     # Quantization": codes [-7, 1, 1, -1, 1, -4]; zero padding to a 128 group.

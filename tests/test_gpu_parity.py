@@ -426,6 +426,29 @@ def test_gemm_large_m_full_chip_f16(asym, awq):
     gemm_case(W, X, "f16", 4, asym, s=s, rows=rows, label="full-chip")
 
 
+@pytest.mark.parametrize("M,xdtype,bits", [(5, "f16", 4), (300, "f16", 4), (300, "bf16", 4), (300, "f16", 3)])
+def test_gemm_leaves_memory_past_y_untouched_and_repeats(M, xdtype, bits):
+    # Every GEMM kernel (direct, register-B, LDS-staged) writes only its
+    # [M, N] output, with ragged tiles at both edges, and gives the same bits
+    # on a second call.
+    rng = np.random.default_rng(M + bits)
+    N, K = 520, 1536
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X32 = rng.standard_normal((M, K)).astype(np.float32)
+    X = gpu_x(X32.astype(np.float16) if xdtype == "f16" else synth.to_bf16_bits(X32), xdtype)
+    packed, scales, zeros = ops.quantize_pack(gpu_f16(W), bits, 128, True)
+    guard = 4096
+    dt = torch.float16 if xdtype == "f16" else torch.bfloat16
+    buf = torch.full((M * N + 2 * guard,), 3.0, dtype=dt, device=DEV)
+    Y = buf[guard: guard + M * N].view(M, N)
+    ops.gemm(X, packed, scales, zeros, N, K, bits, 128, out=Y)
+    first = Y.clone()
+    ops.gemm(X, packed, scales, zeros, N, K, bits, 128, out=Y)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:guard] == 3.0) and torch.all(buf[guard + M * N:] == 3.0)
+    assert torch.equal(first.view(torch.int16), Y.view(torch.int16))
+
+
 def test_gemm_large_m_one_hot_rows_f16():
     # fp16 large-M path: w_hat is rounded once to fp16, so a one-hot row of X
     # returns that rounding bit for bit.

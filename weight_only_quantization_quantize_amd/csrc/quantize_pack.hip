@@ -12,10 +12,11 @@
 // Model on a Laptop", sections "Symmetric Quantization" and "Asymmetric
 // Quantization".)
 //
-// Every decision is one correctly rounded binary32 operation: IEEE division
-// (the build keeps HIP's correctly rounded fp32 divide), rintf = round half to
-// even, fp32 -> fp16 conversion round-to-nearest-even with subnormals, and no
-// FMA contraction in this file.
+// Every decision is one correctly rounded binary32 operation: the quotient
+// of IEEE division (the group's S / qmax and -min / S divide; a weight's w / S
+// comes from the group's reciprocal with two exact fma corrections, equal to
+// the IEEE quotient), rintf = round half to even, fp32 -> fp16 conversion
+// round-to-nearest-even with subnormals, and no FMA contraction in this file.
 //
 // Work split: one thread owns one 32-weight chunk of a row (64 B of fp16 in,
 // 16 B (4-bit) or 12 B (3-bit) of codes out).  For group sizes whose chunk

@@ -10,10 +10,13 @@ streams from HBM rather than from the 256 MB Infinity Cache.
 `value` is the GEMV's effective HBM bandwidth: algorithmic bytes (packed codes
 + fp16 scales + fp16 zeros + x + y) divided by the GEMV kernel's average
 duration.  That duration comes from HIP events recorded on the launch stream
-around each step's back-to-back GEMV burst (events around every single launch
-would add their own ~2 us per launch); the stream is pre-filled with a spin
-kernel before the timed steps so host-side launch latency never shows up as
-GPU idle time inside the events.  The CPU oracle is timed on a bounded sample
+around each step's burst of GEMV_BURST back-to-back GEMVs: a pair of timing
+events costs about 2 us of its own (the first GEMV after an event also starts
+without overlap), so the burst is long enough that this cost stays near 0.1 us
+per launch and the figure agrees with the per-kernel durations of a rocprofv3
+kernel trace.  The stream is pre-filled with a spin kernel before the timed
+steps so host-side launch latency never shows up as GPU idle time inside the
+events.  The CPU oracle is timed on a bounded sample
 of the same workload (cpu_baseline).
 
 The same run also times the other rows of the path on their own workloads
@@ -50,7 +53,7 @@ MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA (no sparsity)
 FP64_PEAK_TFLOPS = 78.6        # MI355X fp64 (vector and matrix)
 MALL_BYTES = 256 << 20
 METRIC = "W4A16 g128 GEMV µs + effective HBM GB/s (% peak) at M=1, K=N=8192"
-GEMV_BURST = 8
+GEMV_BURST = 64
 PREFILL_CYCLES = 40_000_000  # spin kernel that keeps the queue ahead of the host
 
 

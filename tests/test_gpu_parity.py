@@ -391,6 +391,58 @@ def test_gemm_one_hot_rows():
             assert np.array_equal(Y[m].view(np.uint16), w_hat16[:, k].view(np.uint16)), (bits, k)
 
 
+# Small-batch kernel (2 <= M <= 16, 4-bit codes, group 128, K = 2048, 4096 or
+# 8192): the X rows stay in registers while 16-column tiles of codes stream
+# past.  Ragged N (the last tile clamps its loads), 1 to 16 tiles per
+# workgroup, AWQ scales (fp16), symmetric codes, both activation types.
+@pytest.mark.parametrize("M,N,K,xdtype,asym,awq", [
+    (2, 200, 2048, "f16", True, False), (3, 1000, 4096, "bf16", True, False),
+    (4, 4100, 8192, "f16", True, False), (8, 8200, 4096, "f16", False, False),
+    (15, 5000, 2048, "bf16", False, False), (16, 9000, 8192, "f16", True, True),
+    (16, 300, 4096, "f16", False, True), (5, 16, 8192, "bf16", True, False),
+    (9, 65536, 2048, "f16", True, False)])
+def test_gemm_skinny_shapes(M, N, K, xdtype, asym, awq):
+    rng = np.random.default_rng(M * 7 + N + K)
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X32 = rng.standard_normal((M, K)).astype(np.float32)
+    s = None
+    if awq:
+        s = np.exp(rng.uniform(-1.0, 1.0, K)).astype(np.float32)
+        X32[:, rng.choice(K, 16, replace=False)] *= 50.0
+    X = X32.astype(np.float16) if xdtype == "f16" else synth.to_bf16_bits(X32)
+    rows = None
+    if N > 4096:
+        rows = np.concatenate([np.sort(rng.choice(N - 1, 256, replace=False)), [N - 1]])
+    gemm_case(W, X, xdtype, 4, asym, s=s, rows=rows, label="skinny")
+
+
+def test_gemm_skinny_one_hot_rows_and_guard():
+    # Each one-hot row of X returns its column of w_hat rounded once to fp16
+    # (the weights are never rounded on the way), the output is the only
+    # memory written, and a second call gives the same bits.
+    rng = np.random.default_rng(12)
+    N, K = 1000, 4096
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    ks = [0, 7, 127, 128, 2047, 2048, 4095, 1000, 3333, 64, 2100, 4000, 5, 6, 8, 9]
+    M = len(ks)
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), ks] = 1.0
+    packed, scales, zeros = ops.quantize_pack(gpu_f16(W), 4, 128, True)
+    guard = 4096
+    buf = torch.full((M * N + 2 * guard,), 3.0, dtype=torch.float16, device=DEV)
+    Y = buf[guard: guard + M * N].view(M, N)
+    ops.gemm(gpu_f16(X), packed, scales, zeros, N, K, 4, 128, out=Y)
+    first = Y.clone()
+    ops.gemm(gpu_f16(X), packed, scales, zeros, N, K, 4, 128, out=Y)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:guard] == 3.0) and torch.all(buf[guard + M * N:] == 3.0)
+    assert torch.equal(first.view(torch.int16), Y.view(torch.int16))
+    w_hat16 = O.dequantize(O.quantize(W, 4, 128, True)).astype(np.float16)
+    Yh = Y.cpu().numpy()
+    for m, k in enumerate(ks):
+        assert np.array_equal(Yh[m].view(np.uint16), w_hat16[:, k].view(np.uint16)), k
+
+
 # Large M (>= 128) takes the LDS-staged MFMA kernel: ragged M and N tiles,
 # groups that do not divide its K block, AWQ scales, and for fp16 the
 # fallback to the direct kernel when K % 64 != 0.

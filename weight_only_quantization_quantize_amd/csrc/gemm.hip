@@ -482,6 +482,8 @@ hipError_t launch_gemm(const void* X, int xdtype, const float* act_scale, const 
   if (M >= kLdsGemmMinM && (xdtype != 0 || K % 64 == 0))
     return launch_gemm_lds(X, xdtype, act_scale, packed, scales, zeros, M, N, K, bits, group_size, asymmetric, Y,
                            stream);
+  if (gemm_skinny_supported(M, N, K, xdtype, act_scale != nullptr, bits, group_size, scales, zeros))
+    return launch_gemm_skinny(X, xdtype, act_scale, packed, scales, zeros, M, N, K, asymmetric, Y, stream);
   if (bits == 4)
     return asymmetric
                ? launch_asym<4, true>(X, xdtype, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream)

@@ -391,16 +391,21 @@ def test_gemm_one_hot_rows():
             assert np.array_equal(Y[m].view(np.uint16), w_hat16[:, k].view(np.uint16)), (bits, k)
 
 
-# Small-batch kernel (2 <= M <= 16, 4-bit codes, group 128, K = 2048, 4096 or
-# 8192): the X rows stay in registers while 16-column tiles of codes stream
-# past.  Ragged N (the last tile clamps its loads), 1 to 16 tiles per
-# workgroup, AWQ scales (fp16), symmetric codes, both activation types.
+# Small-batch kernel (2 <= M <= 64, 4-bit codes, group 128, K = 2048, 4096 or
+# 8192): 16 X rows stay in registers while 16-column tiles of codes stream
+# past, one workgroup per row tile.  Ragged N (the last tile clamps its
+# loads), ragged M (a partial last row tile, and a row-tile slot past M for
+# 33..48 rows), 1 to 16 tiles per workgroup, column groups with no tile, AWQ
+# scales (fp16), symmetric codes, both activation types.
 @pytest.mark.parametrize("M,N,K,xdtype,asym,awq", [
     (2, 200, 2048, "f16", True, False), (3, 1000, 4096, "bf16", True, False),
     (4, 4100, 8192, "f16", True, False), (8, 8200, 4096, "f16", False, False),
     (15, 5000, 2048, "bf16", False, False), (16, 9000, 8192, "f16", True, True),
     (16, 300, 4096, "f16", False, True), (5, 16, 8192, "bf16", True, False),
-    (9, 65536, 2048, "f16", True, False)])
+    (9, 65536, 2048, "f16", True, False), (17, 1000, 4096, "f16", True, False),
+    (33, 3000, 8192, "bf16", True, False), (48, 600, 2048, "f16", False, True),
+    (64, 5000, 8192, "f16", True, True), (40, 20, 4096, "f16", True, False),
+    (31, 70000, 4096, "bf16", False, False)])
 def test_gemm_skinny_shapes(M, N, K, xdtype, asym, awq):
     rng = np.random.default_rng(M * 7 + N + K)
     W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
@@ -416,15 +421,16 @@ def test_gemm_skinny_shapes(M, N, K, xdtype, asym, awq):
     gemm_case(W, X, xdtype, 4, asym, s=s, rows=rows, label="skinny")
 
 
-def test_gemm_skinny_one_hot_rows_and_guard():
+@pytest.mark.parametrize("M", [16, 41])
+def test_gemm_skinny_one_hot_rows_and_guard(M):
     # Each one-hot row of X returns its column of w_hat rounded once to fp16
     # (the weights are never rounded on the way), the output is the only
     # memory written, and a second call gives the same bits.
-    rng = np.random.default_rng(12)
+    rng = np.random.default_rng(12 + M)
     N, K = 1000, 4096
     W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
     ks = [0, 7, 127, 128, 2047, 2048, 4095, 1000, 3333, 64, 2100, 4000, 5, 6, 8, 9]
-    M = len(ks)
+    ks = (ks + [int(k) for k in rng.choice(K, M, replace=False)])[:M]
     X = np.zeros((M, K), np.float16)
     X[np.arange(M), ks] = 1.0
     packed, scales, zeros = ops.quantize_pack(gpu_f16(W), 4, 128, True)

@@ -1,4 +1,4 @@
-// Small-batch fused dequantize + GEMM (2 <= M <= 16, 4-bit codes, group 128)
+// Small-batch fused dequantize + GEMM (2 <= M <= 64, 4-bit codes, group 128)
 // on gfx950 matrix cores:
 //   Y[m, n] = sum_g S[n,g] * sum_{k in g} x'[m,k] (u[n,k] - Z[n,g]),  x' = X / s.
 //
@@ -11,17 +11,24 @@
 //
 // Work split.  A workgroup is 16 waves; wave w owns the K blocks
 // [w BPW, (w + 1) BPW) of 128 weights (one group each), so K = 2048 BPW
-// (BPW = 1, 2 or 4).  It loads its A fragments (X' rows 0..15, rows >= M as
-// zeros) once: 16 BPW registers per lane.  The workgroup then walks output tiles of 16 columns,
-// tile = blockIdx.x, blockIdx.x + gridDim.x, ...: every wave computes the
-// 16 x 16 partial of its K blocks with v_mfma_f32_16x16x32_{f16,bf16}, the
-// 16 partials meet in LDS (one barrier per tile, double-buffered) and four
-// waves add them in a fixed order and store Y.
+// (BPW = 1, 2 or 4).  It loads its A fragments (16 rows of X', rows >= M as
+// zeros) once: 16 BPW registers per lane.  The workgroup then walks output
+// tiles of 16 columns, tile = g, g + G, ... for its column group g of G:
+// every wave computes the 16 x 16 partial of its K blocks with
+// v_mfma_f32_16x16x32_{f16,bf16}, the 16 partials meet in LDS (one barrier
+// per tile, double-buffered) and four waves add them in a fixed order and
+// store Y.  More than 16 rows are cut into row tiles of 16, one workgroup
+// each, whose workgroups run side by side on one XCD so that the codes they
+// share are fetched from HBM about once.
 //
 // K order inside a block.  Lane (r, q) (r = lane % 16, q = lane / 16) supplies
 // at MFMA step s the 8 slots of K offsets 32 q + 8 s + j (j = 0..7) for both
 // A and B, so each slot is summed once and a lane's codes of the block are one
 // 16-byte chunk of layout v1, word s holding step s.
+//
+// Loads.  Codes and X are read in row-contiguous runs (a load never splits a
+// row's segment over lanes of different rows) and turned into MFMA fragments
+// through a per-wave LDS buffer that only the wave itself touches.
 //
 // Decode.  A code pair becomes the 16-bit floats MAGIC + u (one v_and_or_b32),
 // and per group acc += S (part - (MAGIC + Z) sum x), where sum x over the
@@ -29,9 +36,9 @@
 // workgroup and kept in LDS.  The weights are never rounded; the only
 // roundings are the MFMA's fp32 accumulation and the final conversion of Y.
 //
-// Pipelining.  Each lane's chunk of block b for the next tile is loaded as
-// soon as the current tile's chunk b has been decoded, so one tile of codes is
-// always in flight per wave (16 waves per compute unit).
+// Pipelining.  The next tile's codes, scales and zero points are loaded as
+// soon as the current tile's codes are staged, so one tile is always in
+// flight per wave (16 waves per compute unit).
 #include "woq_device.h"
 #include "woq_internal.h"
 
@@ -47,8 +54,20 @@ constexpr int kSkPitch = 272;         // staged row of 256 bytes + 16 against LD
 template <class XT, int BPW, bool ASYM, bool SCALE>
 __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ s, const uint8_t* __restrict__ packed,
-    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int M, int N, int K,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int M, int N, int K, int rtp,
     uint16_t* __restrict__ Y) {
+  // Workgroup b = x + 8 (rt + rtp z), x < 8: row tile rt (rows 16 rt ..
+  // 16 rt + 15) of column group x + 8 z.  The rtp row tiles of a column group
+  // are 8 apart in dispatch order, so they land on the same XCD and share its
+  // L2: the codes come from HBM about once and the other row tiles read them
+  // from L2 at the same time.
+  const int bx = (int)blockIdx.x & 7, brest = (int)blockIdx.x >> 3;
+  const int rt = brest % rtp, cgroup = bx + 8 * (brest / rtp), ngroups = (int)gridDim.x / rtp;
+  const int row0 = 16 * rt;
+  if (row0 >= M) return;  // a row tile past M: the whole workgroup leaves before any barrier
+  X += (int64_t)row0 * K;
+  Y += (int64_t)row0 * N;
+  M = M - row0 < 16 ? M - row0 : 16;
   // Per wave: a 16-row staging buffer that turns row-contiguous global loads
   // into MFMA fragments; the partials of the cross-wave sum; sum x per block.
   __shared__ __attribute__((aligned(16))) uint8_t stage_all[kSkWaves][16 * kSkPitch];
@@ -123,7 +142,7 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(
       a[b][i] = row < M ? *reinterpret_cast<const u32x4_t*>(X + (int64_t)row * K + kw + kSkBlock * b + 8 * lr)
                         : u32x4_t{0u, 0u, 0u, 0u};
     }
-  int tile = blockIdx.x;
+  int tile = cgroup;
   load_codes(tile);
   load_sz(tile);
 
@@ -171,8 +190,8 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(
   }
 
   const float zsym = 8.0f;  // symmetric 4-bit codes are stored as q + 8
-  for (int it = 0; tile < tiles; tile += gridDim.x, ++it) {
-    const int next = tile + (int)gridDim.x < tiles ? tile + (int)gridDim.x : tiles - 1;
+  for (int it = 0; tile < tiles; tile += ngroups, ++it) {
+    const int next = tile + ngroups < tiles ? tile + ngroups : tiles - 1;
     float S[BPW], C[BPW];
 #pragma unroll
     for (int b = 0; b < BPW; ++b) {
@@ -218,19 +237,23 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(
 template <class XT, int BPW, bool ASYM>
 hipError_t launch_bpw(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
                       int64_t M, int64_t N, int64_t K, void* Y, hipStream_t stream) {
-  const int64_t tiles = (N + 15) / 16;
-  const unsigned grid = (unsigned)(tiles < kSkTargetBlocks ? tiles : kSkTargetBlocks);
+  // Row tiles of 16 (1, 2 or 4 slots; a slot past M exits at once) times
+  // column groups, a multiple of 8 so that every XCD holds whole groups.
+  const int rt = (int)((M + 15) / 16), rtp = rt == 1 ? 1 : (rt == 2 ? 2 : 4);
+  const int64_t tiles = (N + 15) / 16, tiles8 = (tiles + 7) / 8 * 8;
+  const int64_t groups = tiles8 < kSkTargetBlocks / rtp ? tiles8 : kSkTargetBlocks / rtp;
+  const unsigned grid = (unsigned)(groups * rtp);
   constexpr bool kF16 = XT::kMagic2 == F16::kMagic2;  // bf16 with a scale goes to the direct kernel
   if (kF16 && s)
     hipLaunchKernelGGL((gemm_skinny_kernel<XT, BPW, ASYM, kF16>), dim3(grid), dim3(kSkWaves * 64), 0, stream,
                        static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
                        static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N,
-                       (int)K, static_cast<uint16_t*>(Y));
+                       (int)K, rtp, static_cast<uint16_t*>(Y));
   else
     hipLaunchKernelGGL((gemm_skinny_kernel<XT, BPW, ASYM, false>), dim3(grid), dim3(kSkWaves * 64), 0, stream,
                        static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
                        static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N,
-                       (int)K, static_cast<uint16_t*>(Y));
+                       (int)K, rtp, static_cast<uint16_t*>(Y));
   return hipGetLastError();
 }
 
@@ -253,7 +276,7 @@ hipError_t launch_xt(const void* X, const float* s, const void* packed, const vo
 
 bool gemm_skinny_supported(int64_t M, int64_t N, int64_t K, int xdtype, bool act_scale, int bits, int group_size,
                            const void* scales, const void* zeros) {
-  if (M < 2 || M > 16 || N < 1 || bits != 4 || group_size != kSkBlock) return false;
+  if (M < 2 || M > 64 || N < 1 || bits != 4 || group_size != kSkBlock) return false;
   if (K % (kSkWaves * kSkBlock) != 0) return false;
   const int64_t bpw = K / (kSkWaves * kSkBlock);
   if (bpw != 1 && bpw != 2 && bpw != kSkMaxBlocks) return false;

@@ -36,8 +36,8 @@ hipError_t launch_gemm_regb(const void* X, const float* act_scale, const void* p
                             const void* zeros, int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric,
                             void* Y, hipStream_t stream);
 
-// Small-batch GEMM (2 <= M <= 16, 4-bit, group 128, K = 2048 * {1..4}): the
-// X rows stay in registers while 16-column tiles of codes stream past.
+// Small-batch GEMM (2 <= M <= 64, 4-bit, group 128, K = 2048 * {1, 2, 4}):
+// 16 X rows stay in registers while 16-column tiles of codes stream past.
 bool gemm_skinny_supported(int64_t M, int64_t N, int64_t K, int xdtype, bool act_scale, int bits, int group_size,
                            const void* scales, const void* zeros);
 hipError_t launch_gemm_skinny(const void* X, int xdtype, const float* act_scale, const void* packed,

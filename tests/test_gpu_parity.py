@@ -391,9 +391,9 @@ def test_gemm_one_hot_rows():
             assert np.array_equal(Y[m].view(np.uint16), w_hat16[:, k].view(np.uint16)), (bits, k)
 
 
-# Small-batch kernel (2 <= M <= 64, 4-bit codes, group 128, K = 2048, 4096 or
-# 8192): 16 X rows stay in registers while 16-column tiles of codes stream
-# past, one workgroup per row tile.  Ragged N (the last tile clamps its
+# Small-batch kernel (4-bit codes, group 128; 2 <= M <= 16 at K = 2048, 4096
+# or 8192, up to M = 64 at K = 4096 or 8192): 16 X rows stay in registers
+# while 16-column tiles of codes stream past, one workgroup per row tile.  Ragged N (the last tile clamps its
 # loads), ragged M (a partial last row tile, and a row-tile slot past M for
 # 33..48 rows), 1 to 16 tiles per workgroup, column groups with no tile, AWQ
 # scales (fp16), symmetric codes, both activation types.
@@ -403,7 +403,7 @@ def test_gemm_one_hot_rows():
     (15, 5000, 2048, "bf16", False, False), (16, 9000, 8192, "f16", True, True),
     (16, 300, 4096, "f16", False, True), (5, 16, 8192, "bf16", True, False),
     (9, 65536, 2048, "f16", True, False), (17, 1000, 4096, "f16", True, False),
-    (33, 3000, 8192, "bf16", True, False), (48, 600, 2048, "f16", False, True),
+    (33, 3000, 8192, "bf16", True, False), (48, 600, 4096, "f16", False, True),
     (64, 5000, 8192, "f16", True, True), (40, 20, 4096, "f16", True, False),
     (31, 70000, 4096, "bf16", False, False)])
 def test_gemm_skinny_shapes(M, N, K, xdtype, asym, awq):

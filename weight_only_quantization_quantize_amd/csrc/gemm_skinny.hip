@@ -280,6 +280,7 @@ bool gemm_skinny_supported(int64_t M, int64_t N, int64_t K, int xdtype, bool act
   if (K % (kSkWaves * kSkBlock) != 0) return false;
   const int64_t bpw = K / (kSkWaves * kSkBlock);
   if (bpw != 1 && bpw != 2 && bpw != kSkMaxBlocks) return false;
+  if (M > 16 && K < 4096) return false;        // measured: the direct kernel is faster there
   if (xdtype != 0 && act_scale) return false;  // bf16 x / s needs the hi + lo pair: direct kernel
   // 32-bit scale / zero loads when the blocks per wave are even
   if (bpw > 1 && ((reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(zeros)) & 3) != 0) return false;

@@ -305,6 +305,24 @@ def time_rows(torch, ops, synth):
                                     "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
                                     "tflops": round(2 * M * lin.N * lin.K / us / 1e6, 1), "bytes": nb,
                                     "rel_l2_sampled": float(f"{err:.3g}")}
+    # Crossover from the M = 1 GEMV (dot2 on the VALU) to the MFMA kernels on
+    # the same weights: the GEMV per row of X against one GEMM launch.
+    cross = {}
+    for M in (1, 2, 8, 32):
+        lin = synth.c4_small_batch(M, "f16", W=W_np)
+        X = x_tensor(lin.X, "f16")
+        Y = torch.empty(M, lin.N, dtype=X.dtype, device=dev)
+        nb = gemv_bytes(lin.N, lin.K, 4, 128, True, M=M)
+        if M == 1:
+            us = burst_us(torch, [lambda j=j: ops.gemv(X[0], *sets[j % R], lin.N, lin.K, 4, 128, out=Y[0])
+                                  for j in range(4 * R)])
+        else:
+            us = burst_us(torch, [lambda j=j: ops.gemm(X, *sets[j % R], lin.N, lin.K, 4, 128, out=Y)
+                                  for j in range(4 * R)])
+        cross[f"M{M}"] = {"us": round(us, 2), "us_per_row": round(us / M, 2),
+                          "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
+                          "kernel": "gemv (VALU dot2)" if M == 1 else "gemm (MFMA)"}
+    c4["crossover_f16"] = cross
     del sets, W
     rows["c4_small_batch_gemm"] = c4
 

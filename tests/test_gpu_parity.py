@@ -421,6 +421,30 @@ def test_gemm_skinny_shapes(M, N, K, xdtype, asym, awq):
     gemm_case(W, X, xdtype, 4, asym, s=s, rows=rows, label="skinny")
 
 
+def test_gemm_small_batch_with_2_byte_aligned_scales():
+    # The C ABI asks only 2-byte alignment of scales / zeros; the small-batch
+    # kernel's 32-bit loads need 4, so such a call must take another kernel
+    # and still be right.
+    rng = np.random.default_rng(77)
+    M, N, K = 8, 600, 4096
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    packed, scales, zeros = ops.quantize_pack(gpu_f16(W), 4, 128, True)
+    sbuf = torch.empty(scales.numel() + 1, dtype=torch.float16, device=DEV)
+    zbuf = torch.empty(zeros.numel() + 1, dtype=torch.float16, device=DEV)
+    s_odd = sbuf[1:].view(scales.shape)
+    z_odd = zbuf[1:].view(zeros.shape)
+    s_odd.copy_(scales)
+    z_odd.copy_(zeros)
+    assert s_odd.data_ptr() % 4 == 2 and z_odd.data_ptr() % 4 == 2
+    Y = ops.gemm(gpu_f16(X), packed, s_odd, z_odd, N, K, 4, 128)
+    Y_ref = ops.gemm(gpu_f16(X), packed, scales, zeros, N, K, 4, 128)
+    q = O.quantize(W, 4, 128, True)
+    err = O.rel_l2(host(Y), O.gemm(X.astype(np.float64), O.dequantize(q)))
+    assert err <= REL_L2
+    assert O.rel_l2(host(Y), host(Y_ref).astype(np.float64)) <= REL_L2
+
+
 @pytest.mark.parametrize("M", [16, 41])
 def test_gemm_skinny_one_hot_rows_and_guard(M):
     # Each one-hot row of X returns its column of w_hat rounded once to fp16

@@ -130,6 +130,12 @@ __global__ __launch_bounds__(256) void damp_kernel(double* __restrict__ M, int64
   }
 }
 
+// Orders this wave's LDS accesses for the compiler without waiting for them:
+// LDS operations of one wave execute in issue order, so a value one lane
+// writes is seen by every lane's later read.  A workgroup barrier would add an
+// s_waitcnt lgkmcnt(0) and drain every read in flight.
+__device__ inline void wave_sync() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
+
 // Diagonal block of panel p (one wave): Cholesky factor L[P, P] in place in
 // M (strictly upper part set to 0) and its inverse into Y[P, P].
 //  - Factor, right-looking, lane r holding row r in registers: for column j,
@@ -151,16 +157,16 @@ __global__ __launch_bounds__(64) void potrf_inv_kernel(double* __restrict__ M, d
 #pragma unroll
   for (int j = 0; j < kPanel; ++j) {
     if (lane == j) col[j] = __builtin_sqrt(a[j]);
-    __syncthreads();
+    wave_sync();
     const double d = col[j];
     const double l = lane == j ? d : a[j] / d;
     a[j] = lane >= j ? l : 0.0;
-    __syncthreads();
+    wave_sync();
     col[lane] = l;
-    __syncthreads();
+    wave_sync();
 #pragma unroll
     for (int c = j + 1; c < kPanel; ++c) a[c] = __builtin_fma(-l, col[c], a[c]);
-    __syncthreads();
+    wave_sync();
   }
 #pragma unroll
   for (int c = 0; c < kPanel; ++c) {
@@ -168,9 +174,9 @@ __global__ __launch_bounds__(64) void potrf_inv_kernel(double* __restrict__ M, d
     lt[c][lane] = v;
     M[(P0 + lane) * K + P0 + c] = v;
   }
-  __syncthreads();
+  wave_sync();
   rd[lane] = 1.0 / lt[lane][lane];
-  __syncthreads();
+  wave_sync();
   double z[kPanel];
 #pragma unroll
   for (int r = 0; r < kPanel; ++r) z[r] = r == lane ? 1.0 : 0.0;

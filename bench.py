@@ -155,7 +155,7 @@ def write_traffic(prof_dir, copy_mib):
         table.append((k, len(fetch[k]), fk, wk, fk * fetch_scale * 1024, wk * write_scale * 1024))
     gemv = [t for t in table if "gemv_kernel<4, true, woq::F16, false, 4, 4, 2>" in t[0]]
     if len(gemv) != 1:
-        raise SystemExit("the c2 GEMV kernel is not in the counter CSVs")
+        raise SystemExit("the K = N = 8192 GEMV kernel is not in the counter CSVs")
     k, _, fk, wk, rb, wb = gemv[0]
     with open(os.path.join(ROOT, "weight_only_quantization_quantize_amd", "csrc", "gemv.hip"), "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
@@ -226,9 +226,9 @@ def time_rows(torch, ops, synth, checks):
         checks.append(("gemm", row, key, np.ascontiguousarray(lin.W[sel]), lin.X, lin.xdtype, s, host_y(Y)[:, sel]))
 
     # Decode GEMVs of the LLaMA-2-7B linears with their AWQ scales (4-bit asym g128).
-    c3 = {}
+    llama = {}
     for i in range(7):
-        lin = synth.c3_linear(i)
+        lin = synth.llama7b_linear(i)
         W = torch.from_numpy(lin.W).to(dev)
         s = torch.from_numpy(lin.act_scale).to(dev)
         x = torch.from_numpy(lin.X[0]).to(dev)
@@ -239,18 +239,18 @@ def time_rows(torch, ops, synth, checks):
         us = burst_us(torch, [lambda j=j: ops.gemv(x, *sets[j % R], lin.N, lin.K, 4, 128, s, out=y)
                               for j in range(10 * R)])
         sel = np.arange(0, lin.N, max(1, lin.N // 256))
-        c3[lin.name] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
+        llama[lin.name] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
                         "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": nb}
-        record("c3_decode_gemv_awq", lin.name, lin, y[None, :], lin.act_scale, sel)
+        record("llama7b_decode_gemv_awq", lin.name, lin, y[None, :], lin.act_scale, sel)
         del sets, W
-    rows["c3_decode_gemv_awq"] = c3
+    rows["llama7b_decode_gemv_awq"] = llama
 
     # Fused projections: q/k/v (N = 3 x 4096) and gate/up (N = 2 x 11008) share
     # the input and its AWQ scale, so one launch over the stacked rows serves
     # them; compared with the sum of the separate launches above.
     fused = {}
     for name, idx in (("qkv", [0, 1, 2]), ("gate_up", [4, 5])):
-        lins = [synth.c3_linear(i) for i in idx]
+        lins = [synth.llama7b_linear(i) for i in idx]
         K = lins[0].K
         s = torch.from_numpy(lins[0].act_scale).to(dev)
         x = torch.from_numpy(lins[0].X[0]).to(dev)
@@ -260,7 +260,7 @@ def time_rows(torch, ops, synth, checks):
         R = rotate_count(nb)
         sets = [ops.quantize_pack_fused(Ws, 4, 128, True, s) for _ in range(R)]
         us = burst_us(torch, [lambda j=j: ops.gemv_fused(x, *sets[j % R], K, 4, 128, s) for j in range(10 * R)])
-        sep = sum(c3[l.name]["us"] for l in lins)
+        sep = sum(llama[l.name]["us"] for l in lins)
         fused[name] = {"N": N, "K": K, "us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
                        "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": nb,
                        "separate_us_sum": round(sep, 3), "speedup_vs_separate": round(sep / us, 3)}
@@ -268,7 +268,7 @@ def time_rows(torch, ops, synth, checks):
     rows["fused_projection_gemv_awq"] = fused
 
     # Group sizes 32 / 64 / K on the decode shape (M=1, K=N=8192, 4-bit asym).
-    lin = synth.c2_decode()
+    lin = synth.decode_8k()
     W = torch.from_numpy(lin.W).to(dev)
     x = torch.from_numpy(lin.X[0]).to(dev)
     gs = {}
@@ -282,14 +282,14 @@ def time_rows(torch, ops, synth, checks):
                        "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": nb}
         del sets
     del W
-    rows["group_size_gemv_c2"] = gs
+    rows["group_size_gemv_k8192_n8192"] = gs
 
     # Small-batch GEMM, M = 4 / 16 / 64, K = 8192, N = 28672.
-    c4 = {}
+    small = {}
     W, W_np = None, None
     for xdtype in ("f16", "bf16"):
         for M in (4, 16, 64):
-            lin = synth.c4_small_batch(M, xdtype, W=W_np)
+            lin = synth.small_batch(M, xdtype, W=W_np)
             W_np = lin.W
             if W is None:
                 W = torch.from_numpy(lin.W).to(dev)
@@ -302,15 +302,15 @@ def time_rows(torch, ops, synth, checks):
             us = burst_us(torch, [lambda j=j: ops.gemm(X, *sets[j % R], lin.N, lin.K, 4, 128, out=Y)
                                   for j in range(4 * R)])
             sel = np.arange(0, lin.N, lin.N // 128)
-            c4[f"M{M}_{xdtype}"] = {"us": round(us, 2), "gbs": round(nb / us / 1e3, 1),
+            small[f"M{M}_{xdtype}"] = {"us": round(us, 2), "gbs": round(nb / us / 1e3, 1),
                                     "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
                                     "tflops": round(2 * M * lin.N * lin.K / us / 1e6, 1), "bytes": nb}
-            record("c4_small_batch_gemm", f"M{M}_{xdtype}", lin, Y, None, sel)
+            record("small_batch_gemm_k8192_n28672", f"M{M}_{xdtype}", lin, Y, None, sel)
     # Crossover from the M = 1 GEMV (dot2 on the VALU) to the MFMA kernels on
     # the same weights: the GEMV per row of X against one GEMM launch.
     cross = {}
     for M in (1, 2, 8, 32):
-        lin = synth.c4_small_batch(M, "f16", W=W_np)
+        lin = synth.small_batch(M, "f16", W=W_np)
         X = x_tensor(lin.X, "f16")
         Y = torch.empty(M, lin.N, dtype=X.dtype, device=dev)
         nb = gemv_bytes(lin.N, lin.K, 4, 128, True, M=M)
@@ -323,15 +323,15 @@ def time_rows(torch, ops, synth, checks):
         cross[f"M{M}"] = {"us": round(us, 2), "us_per_row": round(us / M, 2),
                           "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4),
                           "kernel": "gemv (VALU dot2)" if M == 1 else "gemm (MFMA)"}
-    c4["crossover_f16"] = cross
+    small["crossover_f16"] = cross
     del sets, W
-    rows["c4_small_batch_gemm"] = c4
+    rows["small_batch_gemm_k8192_n28672"] = small
 
     # Prefill GEMM, M = 2048, K = 4096, N = 11008.
-    lin = synth.c5_prefill()
+    lin = synth.prefill()
     W = torch.from_numpy(lin.W).to(dev)
     sets = [ops.quantize_pack(W, 4, 128, True) for _ in range(4)]
-    c5 = {}
+    pre = {}
     for xdtype in ("f16", "bf16"):
         X = torch.from_numpy(lin.X).to(dev)
         if xdtype == "bf16":
@@ -344,15 +344,15 @@ def time_rows(torch, ops, synth, checks):
                  "frac_mfma": round(fl / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4), "flop": fl}
         if xdtype == "f16":
             sel = np.arange(0, lin.N, lin.N // 96)
-            record("c5_prefill_gemm", xdtype, lin, Y, None, sel)
-        c5[xdtype] = entry
+            record("prefill_gemm_m2048_k4096_n11008", xdtype, lin, Y, None, sel)
+        pre[xdtype] = entry
     del sets, W
-    rows["c5_prefill_gemm"] = c5
+    rows["prefill_gemm_m2048_k4096_n11008"] = pre
 
     # AWQ exponent search (20 exponents) for the q_proj shape on 512
     # calibration tokens with 1% outlier channels: per exponent one scale,
     # quantize_pack, prefill-size GEMM and error reduction.
-    lin = synth.c3_linear(0)
+    lin = synth.llama7b_linear(0)
     ch = lin.extra["channels"]
     Xc = torch.from_numpy(synth.to_f16(synth.activations_f32(synth.CALIBRATION_TOKENS, lin.K, 3200, ch))).to(dev)
     Wq = torch.from_numpy(lin.W).to(dev)
@@ -527,7 +527,7 @@ def main():
     _lib.load()
     torch.cuda.set_device(dev)
     bits, G, asym = 4, 128, True
-    lin = synth.c2_decode()
+    lin = synth.decode_8k()
     N, K = lin.N, lin.K
 
     # Resident inputs: rotated fp16 weight copies and packed sets.

@@ -68,8 +68,8 @@ def assert_pack_equal(gpu, ref):
 @pytest.mark.parametrize("bits", [3, 4])
 @pytest.mark.parametrize("asym", [False, True])
 def test_quantize_pack_small_workload(bits, asym):
-    lin = synth.c1_small()
-    _say(f"quantize_pack c1 bits={bits} asym={asym}")
+    lin = synth.decode_1k()
+    _say(f"quantize_pack 1024x1024 bits={bits} asym={asym}")
     gpu, ref = quantize_both(lin.W, bits, 128, asym)
     assert_pack_equal(gpu, ref)
 
@@ -77,8 +77,8 @@ def test_quantize_pack_small_workload(bits, asym):
 @pytest.mark.parametrize("bits", [3, 4])
 @pytest.mark.parametrize("asym", [False, True])
 def test_quantize_pack_decode_shape(bits, asym):
-    lin = synth.c2_decode()
-    _say(f"quantize_pack c2 8192x8192 bits={bits} asym={asym}")
+    lin = synth.decode_8k()
+    _say(f"quantize_pack 8192x8192 bits={bits} asym={asym}")
     gpu, ref = quantize_both(lin.W, bits, 128, asym)
     assert_pack_equal(gpu, ref)
 
@@ -86,8 +86,8 @@ def test_quantize_pack_decode_shape(bits, asym):
 @pytest.mark.parametrize("i", [0, 4, 6])
 @pytest.mark.parametrize("bits", [3, 4])
 def test_quantize_pack_awq_fold(i, bits):
-    lin = synth.c3_linear(i)
-    _say(f"quantize_pack c3 {lin.name} bits={bits} with AWQ scale")
+    lin = synth.llama7b_linear(i)
+    _say(f"quantize_pack {lin.name} bits={bits} with AWQ scale")
     gpu, ref = quantize_both(lin.W, bits, 128, True, lin.act_scale)
     assert_pack_equal(gpu, ref)
 
@@ -175,7 +175,7 @@ def test_quantize_pack_worked_example():
 
 
 def test_quantize_pack_leaves_memory_past_the_outputs_untouched():
-    lin = synth.c1_small()
+    lin = synth.decode_1k()
     N, K = lin.W.shape
     guard = 4096
     packed = torch.full((N * K // 2 + guard,), 0xA5, dtype=torch.uint8, device=DEV)
@@ -196,7 +196,7 @@ def test_quantize_pack_leaves_memory_past_the_outputs_untouched():
 @pytest.mark.parametrize("bits", [3, 4])
 @pytest.mark.parametrize("asym", [False, True])
 def test_dequantize_exact(bits, asym):
-    lin = synth.c1_small()
+    lin = synth.decode_1k()
     gpu, ref = quantize_both(lin.W, bits, 128, asym)
     w_hat = ops.dequantize(*gpu, 1024, 1024, bits, 128).cpu().numpy().astype(np.float64)
     assert np.array_equal(w_hat, O.dequantize(ref[3]))
@@ -223,24 +223,24 @@ def gemv_case(lin, bits, asym, xdtype="f16", G=128, use_scale=True):
 @pytest.mark.parametrize("asym", [False, True])
 @pytest.mark.parametrize("xdtype", ["f16", "bf16"])
 def test_gemv_small_workload(bits, asym, xdtype):
-    gemv_case(synth.c1_small(), bits, asym, xdtype)
+    gemv_case(synth.decode_1k(), bits, asym, xdtype)
 
 
 @pytest.mark.parametrize("bits", [3, 4])
 @pytest.mark.parametrize("asym", [False, True])
 def test_gemv_decode_shape(bits, asym):
-    gemv_case(synth.c2_decode(), bits, asym)
+    gemv_case(synth.decode_8k(), bits, asym)
 
 
 @pytest.mark.parametrize("i", range(7))
 @pytest.mark.parametrize("bits", [3, 4])
 def test_gemv_llama_linears_with_awq(i, bits):
-    gemv_case(synth.c3_linear(i), bits, True)
+    gemv_case(synth.llama7b_linear(i), bits, True)
 
 
 @pytest.mark.parametrize("i", range(7))
 def test_gemv_llama_linears_with_awq_bf16(i):
-    gemv_case(synth.c3_linear(i), 4, True, "bf16")
+    gemv_case(synth.llama7b_linear(i), 4, True, "bf16")
 
 
 # Fused projections: q/k/v (and gate/up) read the same input and AWQ scale,
@@ -248,7 +248,7 @@ def test_gemv_llama_linears_with_awq_bf16(i):
 @pytest.mark.parametrize("which,bits,asym", [("qkv", 4, True), ("gate_up", 4, True), ("qkv", 3, False)])
 def test_fused_projection_gemv(which, bits, asym):
     idx = [0, 1, 2] if which == "qkv" else [4, 5]
-    lins = [synth.c3_linear(i) for i in idx]
+    lins = [synth.llama7b_linear(i) for i in idx]
     K = lins[0].K
     x, s = lins[0].X[0], lins[0].act_scale  # the shared input and its scale
     Ws = [gpu_f16(l.W) for l in lins]
@@ -288,7 +288,7 @@ def test_gemv_ragged_shapes(N, K):
 
 @pytest.mark.parametrize("G", [32, 64, 256, 4096])
 def test_gemv_group_sizes(G):
-    lin = synth.c3_linear(0)
+    lin = synth.llama7b_linear(0)
     gemv_case(lin, 4, True, G=G)
     gemv_case(lin, 3, False, G=G)
 
@@ -296,7 +296,7 @@ def test_gemv_group_sizes(G):
 @pytest.mark.parametrize("bits", [3, 4])
 def test_gemv_one_hot_columns(bits):
     # x = e_k isolates column k of w_hat: every layout position decodes right
-    lin = synth.c1_small()
+    lin = synth.decode_1k()
     gpu, ref = quantize_both(lin.W, bits, 128, True)
     w_hat16 = O.dequantize(ref[3]).astype(np.float16)
     for k in list(range(0, 40)) + [127, 128, 511, 1000, 1023]:
@@ -307,7 +307,7 @@ def test_gemv_one_hot_columns(bits):
 
 
 def test_gemv_is_deterministic():
-    lin = synth.c1_small()
+    lin = synth.decode_1k()
     gpu, _ = quantize_both(lin.W, 4, 128, True)
     a = ops.gemv(gpu_f16(lin.X[0]), *gpu, 1024, 1024).cpu().numpy()
     b = ops.gemv(gpu_f16(lin.X[0]), *gpu, 1024, 1024).cpu().numpy()
@@ -362,14 +362,14 @@ def test_gemm_group_sizes(G):
 
 
 def test_gemm_awq_scale():
-    lin = synth.c3_linear(6)
+    lin = synth.llama7b_linear(6)
     X = synth.to_f16(synth.activations_f32(8, lin.K, 77, lin.extra["channels"]))
     gemm_case(lin.W[:300], X, "f16", 4, True, s=lin.act_scale, label="awq")
 
 
 @pytest.mark.parametrize("M", [8, 64])
 def test_gemm_awq_scale_bf16(M):
-    lin = synth.c3_linear(6)
+    lin = synth.llama7b_linear(6)
     X = synth.to_bf16_bits(synth.activations_f32(M, lin.K, 78, lin.extra["channels"]))
     gemm_case(lin.W[:300], X, "bf16", 4, True, s=lin.act_scale, label="awq-bf16")
 
@@ -550,17 +550,17 @@ def test_gemm_large_m_one_hot_rows_f16():
 @pytest.mark.parametrize("M", [4, 16, 64])
 @pytest.mark.parametrize("xdtype", ["f16", "bf16"])
 def test_gemm_small_batch_full_size_sampled(M, xdtype):
-    lin = synth.c4_small_batch(M, xdtype)
+    lin = synth.small_batch(M, xdtype)
     rows = np.sort(np.random.default_rng(M).choice(lin.N, 192, replace=False))
     rows = np.concatenate([rows, [lin.N - 1]])
-    gemm_case(lin.W, lin.X, xdtype, 4, True, rows=rows, label="c4")
+    gemm_case(lin.W, lin.X, xdtype, 4, True, rows=rows, label="small-batch")
 
 
 def test_gemm_prefill_full_size_sampled():
-    lin = synth.c5_prefill()
+    lin = synth.prefill()
     rows = np.sort(np.random.default_rng(5).choice(lin.N, 96, replace=False))
     rows = np.concatenate([rows, [lin.N - 1]])
-    gemm_case(lin.W, lin.X, "f16", 4, True, rows=rows, label="c5")
+    gemm_case(lin.W, lin.X, "f16", 4, True, rows=rows, label="prefill")
 
 
 # ---------------------------------------------------------------------------

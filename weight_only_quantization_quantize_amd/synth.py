@@ -21,7 +21,9 @@ calibration text) that are not available here:
   (the mean-|x| statistic recorded by forward hooks in "MIT 6.5940 Lab 4 +
   Lab 5", Lab 4 setup).
 
-Seeds: workload c, tensor t -> seed 1000*c + t (see ``WORKLOADS``).
+Seeds: each workload draws from its own block of seeds (1000s for the
+1024 x 1024 decode shape, 2000s for 8192 x 8192, 3000s for the LLaMA-2-7B
+linears, 4000s for the small batch, 5000s for the prefill; see ``WORKLOADS``).
 """
 from __future__ import annotations
 
@@ -139,17 +141,17 @@ class Linear:
     extra: Dict = field(default_factory=dict)
 
 
-def c1_small() -> Linear:
+def decode_1k() -> Linear:
     """M=1, K=N=1024, W ~ N(0, 0.02) (seed 1001), x ~ N(0, 1) (seed 1002)."""
-    return Linear("c1_1x1024x1024", 1, 1024, 1024, weights(1024, 1024, 1001), activations(1, 1024, 1002))
+    return Linear("decode_1x1024x1024", 1, 1024, 1024, weights(1024, 1024, 1001), activations(1, 1024, 1002))
 
 
-def c2_decode(N: int = 8192, K: int = 8192) -> Linear:
+def decode_8k(N: int = 8192, K: int = 8192) -> Linear:
     """Decode GEMV M=1, K=N=8192: N(0,0.02) weights (seed 2001) with 0.1% of
     entries (positions seed 2002) redrawn from N(0, 0.5) (seed 2003); x ~ N(0,1)
     (seed 2004)."""
     W = weights_with_outliers(N, K, 2001, 2002, 2003)
-    return Linear(f"c2_1x{K}x{N}", 1, N, K, W, activations(1, K, 2004))
+    return Linear(f"decode_1x{K}x{N}", 1, N, K, W, activations(1, K, 2004))
 
 
 # LLaMA-2-7B decoder linears as (name, N, K): q, k, v, o, gate, up, down.
@@ -164,7 +166,7 @@ LLAMA7B_LINEARS: List[Tuple[str, int, int]] = [
 ]
 
 
-def c3_linear(i: int, with_weights: bool = True) -> Linear:
+def llama7b_linear(i: int, with_weights: bool = True) -> Linear:
     """LLaMA-2-7B-shaped decode linear i (0..6): W ~ N(0, 0.02) (seed 3000+10i);
     x ~ N(0,1) with 1% of channels x50 (channels and values seed 3100+i); AWQ
     scale from 512 calibration tokens with the same outlier channels (seed 3200+i)."""
@@ -173,30 +175,30 @@ def c3_linear(i: int, with_weights: bool = True) -> Linear:
     x32 = activations_f32(1, K, 3100 + i, ch)
     s = awq_scale(K, 3200 + i, ch)
     W = weights(N, K, 3000 + 10 * i) if with_weights else None
-    return Linear(f"c3_{name}_1x{K}x{N}", 1, N, K, W, to_f16(x32), "f16", s, {"channels": ch})
+    return Linear(f"{name}_1x{K}x{N}", 1, N, K, W, to_f16(x32), "f16", s, {"channels": ch})
 
 
-def c4_small_batch(M: int, xdtype: str = "f16", N: int = 28672, K: int = 8192,
-                   W: Optional[np.ndarray] = None) -> Linear:
+def small_batch(M: int, xdtype: str = "f16", N: int = 28672, K: int = 8192,
+                W: Optional[np.ndarray] = None) -> Linear:
     """Small-batch GEMM, M in {4, 16, 64}, K=8192, N=28672: W ~ N(0,0.02)
     (seed 4001; pass a previous call's W to skip regenerating it), X ~ N(0,1)
     (seed 4002) stored as fp16 or bf16."""
     W = weights(N, K, 4001) if W is None else W
-    return Linear(f"c4_{M}x{K}x{N}_{xdtype}", M, N, K, W, activations(M, K, 4002, xdtype), xdtype)
+    return Linear(f"small_batch_{M}x{K}x{N}_{xdtype}", M, N, K, W, activations(M, K, 4002, xdtype), xdtype)
 
 
-def c5_prefill(M: int = 2048, N: int = 11008, K: int = 4096) -> Linear:
+def prefill(M: int = 2048, N: int = 11008, K: int = 4096) -> Linear:
     """Prefill GEMM M=2048, K=4096, N=11008: X ~ N(0,1) with 1% of channels x50
     (seed 5001), W ~ N(0, 0.02) (seed 5002)."""
     ch = outlier_channels(K, 5001)
     X = to_f16(activations_f32(M, K, 5001, ch))
-    return Linear(f"c5_{M}x{K}x{N}", M, N, K, weights(N, K, 5002), X, "f16", None, {"channels": ch})
+    return Linear(f"prefill_{M}x{K}x{N}", M, N, K, weights(N, K, 5002), X, "f16", None, {"channels": ch})
 
 
 WORKLOADS = {
-    "c1": "M=1 K=N=1024, 4-bit asymmetric g128",
-    "c2": "M=1 K=N=8192 decode GEMV, 3/4-bit, symmetric and asymmetric, g128",
-    "c3": "LLaMA-2-7B decode linears at M=1 with AWQ scale, 3/4-bit g128",
-    "c4": "M in {4,16,64}, K=8192, N=28672, fp16/bf16 activations, 4-bit asymmetric g128",
-    "c5": "M=2048, K=4096, N=11008 prefill GEMM, 4-bit asymmetric g128",
+    "decode_1k": "M=1 K=N=1024, 4-bit asymmetric g128",
+    "decode_8k": "M=1 K=N=8192 decode GEMV, 3/4-bit, symmetric and asymmetric, g128",
+    "llama7b_linear": "LLaMA-2-7B decode linears at M=1 with AWQ scale, 3/4-bit g128",
+    "small_batch": "M in {4,16,64}, K=8192, N=28672, fp16/bf16 activations, 4-bit asymmetric g128",
+    "prefill": "M=2048, K=4096, N=11008 prefill GEMM, 4-bit asymmetric g128",
 }

@@ -167,8 +167,11 @@ woq_status woq_dequantize(const void* packed, const void* scales, const void* ze
  *                alpha with the smallest loss, ready to pass as act_scale
  *   best_index : out, int32 [1] (device): that alpha's index
  *   workspace  : device scratch of woq_awq_search_workspace_bytes(...) bytes,
- *                256-byte aligned, owned by the caller; holds one packed set,
- *                the reference output X W^T (fp32) and the quantized one.
+ *                256-byte aligned, owned by the caller; holds the reference
+ *                output X W^T (fp32) and, for each exponent of one batched
+ *                GEMM launch (up to 8 where the GEMM is the register-B
+ *                kernel, else 1), a scale vector, a packed set and the
+ *                quantized output.
  * The loss uses the library's own quantize_pack and GEMM (so the quantized
  * output is rounded to fp16 as any other call's), an fp32 reference output
  * and an fp64 sum.  Asynchronous on stream; returns WOQ_ERR_INVALID_ARGUMENT

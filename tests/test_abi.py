@@ -184,13 +184,25 @@ def test_awq_search_rejects(lib, kw, needle):
     assert needle in lib.woq_last_error().decode()
 
 
+def _awq_parts(T, N, K, bits, B):
+    # channel means, B scale vectors, B packed sets with fp16 scales and
+    # zeros, the fp32 reference output, B fp16 quantized outputs, fp64
+    # partial sums: all 256-byte padded
+    parts = [8 * K, 4 * K * B, N * K * bits // 8 * B, 2 * N * (K // 128) * B, 2 * N * (K // 128) * B, 4 * T * N,
+             2 * T * N * B, 8 * 1024]
+    return sum((p + 255) // 256 * 256 for p in parts)
+
+
 def test_awq_search_workspace_size(lib):
-    # one packed set, fp16 scales and zeros, fp32 reference and fp16 quantized
-    # outputs, channel means and scales, fp64 partial sums: all 256-byte padded
+    # 4-bit, fp16, K % 64 == 0 and M >= 128 with few tiles: the register-B
+    # GEMM, batched over min(8, ceil(512 / tiles)) exponents; other quantizers
+    # and shapes evaluate one exponent at a time.
     T, N, K = 128, 64, 256
-    need = lib.woq_awq_search_workspace_bytes(T, N, K, 4, 128, 1)
-    parts = [8 * K, 4 * K, N * K // 2, 2 * N * 2, 2 * N * 2, 4 * T * N, 2 * T * N, 8 * 1024]
-    assert need == sum((p + 255) // 256 * 256 for p in parts)
+    assert lib.woq_awq_search_workspace_bytes(T, N, K, 4, 128, 1) == _awq_parts(T, N, K, 4, 8)
+    assert lib.woq_awq_search_workspace_bytes(T, N, K, 3, 128, 1) == _awq_parts(T, N, K, 3, 1)
+    assert lib.woq_awq_search_workspace_bytes(64, N, K, 4, 128, 1) == _awq_parts(64, N, K, 4, 1)
+    # 512 tokens x 4096 x 11008: 4 x 43 = 172 tiles -> 3 exponents per launch
+    assert lib.woq_awq_search_workspace_bytes(512, 11008, 4096, 4, 128, 1) == _awq_parts(512, 11008, 4096, 4, 3)
     assert lib.woq_awq_search_workspace_bytes(0, N, K, 4, 128, 1) == 0
     assert lib.woq_awq_search_workspace_bytes(T, N, K, 5, 128, 1) == 0
 

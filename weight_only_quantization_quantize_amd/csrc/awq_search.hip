@@ -11,9 +11,12 @@
 //
 // The loop over alpha runs on the host and only enqueues work: per alpha one
 // scale kernel, the library's quantize_pack and GEMM, and a two-pass
-// deterministic reduction of the squared error in fp64.  The reference output
-// X W^T (fp32, from a dense fp16 MFMA kernel) and the channel means (fp64) are
-// computed once.  Everything lives in the caller's workspace.
+// deterministic reduction of the squared error in fp64.  Where the GEMM is
+// the register-B kernel, the products of up to 8 alphas run as one batched
+// launch (the same kernel per tile, so the same outputs), which fills the
+// compute units that one product's tiles would leave idle.  The reference
+// output X W^T (fp32, from a dense fp16 MFMA kernel) and the channel means
+// (fp64) are computed once.  Everything lives in the caller's workspace.
 #include "woq_device.h"
 #include "woq_internal.h"
 
@@ -25,14 +28,28 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 constexpr double kScaleFloor = 1e-4;
 constexpr int kPartials = 1024;  // blocks of the first reduction pass
 
-// m[k] = mean over t of |x[t, k]|, summed in fp64 (exact for the sizes used:
-// fp16 magnitudes added in fp64), divided once.
-__global__ void channel_mean_kernel(const uint16_t* __restrict__ X, int T, int K, double* __restrict__ m) {
-  const int k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= K) return;
+// m[k] = mean over t of |x[t, k]|, summed in fp64 and divided once.  Every
+// fp16 magnitude is an integer multiple of 2^-24 below 2^16, so sums of fewer
+// than 8192 of them are exact in fp64 in any order.  A workgroup takes 64
+// channels; its 16 waves take every 16th token and meet in LDS.
+constexpr int kMeanChannels = 64, kMeanSlices = 16;
+__global__ __launch_bounds__(kMeanChannels * kMeanSlices) void channel_mean_kernel(const uint16_t* __restrict__ X,
+                                                                                   int T, int K,
+                                                                                   double* __restrict__ m) {
+  __shared__ double part[kMeanSlices][kMeanChannels];
+  const int c = threadIdx.x % kMeanChannels, sl = threadIdx.x / kMeanChannels;
+  const int k = blockIdx.x * kMeanChannels + c;
+  const int kk = k < K ? k : K - 1;
   double acc = 0.0;
-  for (int t = 0; t < T; ++t) acc += fabs((double)half_bits_to_f32(X[(int64_t)t * K + k]));
-  m[k] = acc / T;
+  for (int t = sl; t < T; t += kMeanSlices) acc += fabs((double)half_bits_to_f32(X[(int64_t)t * K + kk]));
+  part[sl][c] = acc;
+  __syncthreads();
+  if (sl == 0 && k < K) {
+    double v = 0.0;
+#pragma unroll
+    for (int j = 0; j < kMeanSlices; ++j) v += part[j][c];
+    m[k] = v / T;
+  }
 }
 
 // s[k] = fl32(max(m[k], floor)^alpha).
@@ -59,7 +76,23 @@ __global__ __launch_bounds__(256) void dense_ref_kernel(const uint16_t* __restri
   float16_t acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  for (int k = 0; k < K; k += 16) {
+  // 8 steps of operands loaded before their MFMAs (K % 128 == 0 here, the
+  // remainder one step at a time); the MFMAs run in K order either way.
+  constexpr int kU = 8;
+  int k = 0;
+  for (; k + 16 * kU <= K; k += 16 * kU) {
+    u32x4_t a[kU], b[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      a[u] = *reinterpret_cast<const u32x4_t*>(xa + k + 16 * u);
+      b[u] = *reinterpret_cast<const u32x4_t*>(wb + k + 16 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a[u]), __builtin_bit_cast(half8_t, b[u]),
+                                                   acc, 0, 0, 0);
+  }
+  for (; k < K; k += 16) {
     const u32x4_t a = *reinterpret_cast<const u32x4_t*>(xa + k);
     const u32x4_t b = *reinterpret_cast<const u32x4_t*>(wb + k);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), acc,
@@ -123,12 +156,28 @@ __global__ void awq_select_kernel(const double* __restrict__ losses, int n_grid,
 
 constexpr size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Alphas per batched GEMM launch: enough register-B tiles (128 x 256) for two
+// workgroups on each of the 256 compute units, at most 8; 1 where the GEMM is
+// another kernel.
+int awq_batch(int64_t T, int64_t N, int64_t K, int bits) {
+  if (!gemm_uses_regb(T, N, K, bits, 0)) return 1;
+  const int64_t tiles = ((T + 127) / 128) * ((N + 255) / 256);
+  const int64_t b = (512 + tiles - 1) / tiles;
+  return (int)(b > 8 ? 8 : b);
+}
+
 struct AwqLayout {
+  int batch;
   size_t m, s, packed, scales, zeros, yref, yq, partial, total;
+  size_t packed_bytes, sz_elems, yq_elems;  // per batch entry
 };
 
 AwqLayout awq_layout(int64_t T, int64_t N, int64_t K, int bits, int G, bool asym) {
   AwqLayout L{};
+  L.batch = awq_batch(T, N, K, bits);
+  L.packed_bytes = (size_t)N * K * bits / 8;  // a multiple of 16 (K % 32 == 0)
+  L.sz_elems = (size_t)N * (K / G);
+  L.yq_elems = (size_t)T * N;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -136,12 +185,12 @@ AwqLayout awq_layout(int64_t T, int64_t N, int64_t K, int bits, int G, bool asym
     return at;
   };
   L.m = take(sizeof(double) * K);
-  L.s = take(sizeof(float) * K);
-  L.packed = take((size_t)N * K * bits / 8);
-  L.scales = take(sizeof(uint16_t) * N * (K / G));
-  L.zeros = take(asym ? sizeof(uint16_t) * N * (K / G) : 0);
+  L.s = take(sizeof(float) * K * L.batch);
+  L.packed = take(L.packed_bytes * L.batch);
+  L.scales = take(sizeof(uint16_t) * L.sz_elems * L.batch);
+  L.zeros = take(asym ? sizeof(uint16_t) * L.sz_elems * L.batch : 0);
   L.yref = take(sizeof(float) * T * N);
-  L.yq = take(sizeof(uint16_t) * T * N);
+  L.yq = take(sizeof(uint16_t) * L.yq_elems * L.batch);
   L.partial = take(sizeof(double) * kPartials);
   L.total = off;
   return L;
@@ -168,33 +217,44 @@ hipError_t launch_awq_search(const void* X, const void* W, int64_t T, int64_t N,
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   double* m = reinterpret_cast<double*>(ws + L.m);
   float* s = reinterpret_cast<float*>(ws + L.s);
-  void* packed = ws + L.packed;
-  void* scales = ws + L.scales;
-  void* zeros = asymmetric ? ws + L.zeros : nullptr;
+  uint8_t* packed = ws + L.packed;
+  uint16_t* scales = reinterpret_cast<uint16_t*>(ws + L.scales);
+  uint16_t* zeros = asymmetric ? reinterpret_cast<uint16_t*>(ws + L.zeros) : nullptr;
   float* yref = reinterpret_cast<float*>(ws + L.yref);
-  void* yq = ws + L.yq;
+  uint16_t* yq = reinterpret_cast<uint16_t*>(ws + L.yq);
   double* partial = reinterpret_cast<double*>(ws + L.partial);
   const uint16_t* X16 = static_cast<const uint16_t*>(X);
   const uint16_t* W16 = static_cast<const uint16_t*>(W);
 
   const unsigned kblocks = (unsigned)((K + 255) / 256);
-  hipLaunchKernelGGL(channel_mean_kernel, dim3(kblocks), dim3(256), 0, stream, X16, (int)T, (int)K, m);
+  hipLaunchKernelGGL(channel_mean_kernel, dim3((unsigned)((K + kMeanChannels - 1) / kMeanChannels)),
+                     dim3(kMeanChannels * kMeanSlices), 0, stream, X16, (int)T, (int)K, m);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = launch_dense_ref(X16, W16, T, N, K, yref, stream)) != hipSuccess) return e;
-  for (int i = 0; i < n_grid; ++i) {
-    hipLaunchKernelGGL(awq_scale_kernel, dim3(kblocks), dim3(256), 0, stream, m, (double)i / n_grid, (int)K, s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_quantize_pack(W, s, N, K, bits, group_size, asymmetric, packed, scales, zeros, stream)) !=
-        hipSuccess)
-      return e;
-    if ((e = launch_gemm(X, 0, s, packed, scales, zeros, T, N, K, bits, group_size, asymmetric, yq, stream)) !=
-        hipSuccess)
-      return e;
-    hipLaunchKernelGGL(sqdiff_partial_kernel, dim3(kPartials), dim3(256), 0, stream, yref,
-                       static_cast<const uint16_t*>(yq), T * N, partial);
-    hipLaunchKernelGGL(sqdiff_finish_kernel, dim3(1), dim3(256), 0, stream, partial, losses + i);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int i0 = 0; i0 < n_grid; i0 += L.batch) {
+    const int nb = n_grid - i0 < L.batch ? n_grid - i0 : L.batch;
+    for (int j = 0; j < nb; ++j) {
+      float* sj = s + (int64_t)j * K;
+      hipLaunchKernelGGL(awq_scale_kernel, dim3(kblocks), dim3(256), 0, stream, m, (double)(i0 + j) / n_grid, (int)K,
+                         sj);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = launch_quantize_pack(W, sj, N, K, bits, group_size, asymmetric, packed + j * L.packed_bytes,
+                                    scales + j * L.sz_elems, zeros ? zeros + j * L.sz_elems : nullptr, stream)) !=
+          hipSuccess)
+        return e;
+    }
+    e = L.batch > 1 ? launch_gemm_regb_batched(X, s, K, packed, (int64_t)L.packed_bytes, scales, zeros,
+                                               (int64_t)L.sz_elems, T, N, K, group_size, asymmetric, yq,
+                                               (int64_t)L.yq_elems, nb, stream)
+                    : launch_gemm(X, 0, s, packed, scales, zeros, T, N, K, bits, group_size, asymmetric, yq, stream);
+    if (e != hipSuccess) return e;
+    for (int j = 0; j < nb; ++j) {
+      hipLaunchKernelGGL(sqdiff_partial_kernel, dim3(kPartials), dim3(256), 0, stream, yref,
+                         static_cast<const uint16_t*>(yq + j * L.yq_elems), T * N, partial);
+      hipLaunchKernelGGL(sqdiff_finish_kernel, dim3(1), dim3(256), 0, stream, partial, losses + i0 + j);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   hipLaunchKernelGGL(awq_select_kernel, dim3(kblocks), dim3(256), 0, stream, losses, n_grid, m, (int)K, best_scale,
                      best_index);

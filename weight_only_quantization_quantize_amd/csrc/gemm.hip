@@ -474,10 +474,14 @@ static bool lds_tiles_fill_chip(int64_t M, int64_t N) {
   return tiles * 100 >= rounds * 256 * 95;
 }
 
+bool gemm_uses_regb(int64_t M, int64_t N, int64_t K, int bits, int xdtype) {
+  return M >= kLdsGemmMinM && xdtype == 0 && bits == 4 && K % 64 == 0 && !lds_tiles_fill_chip(M, N);
+}
+
 hipError_t launch_gemm(const void* X, int xdtype, const float* act_scale, const void* packed, const void* scales,
                        const void* zeros, int64_t M, int64_t N, int64_t K, int bits, int group_size, bool asymmetric,
                        void* Y, hipStream_t stream) {
-  if (M >= kLdsGemmMinM && xdtype == 0 && bits == 4 && K % 64 == 0 && !lds_tiles_fill_chip(M, N))
+  if (gemm_uses_regb(M, N, K, bits, xdtype))
     return launch_gemm_regb(X, act_scale, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, stream);
   if (M >= kLdsGemmMinM && (xdtype != 0 || K % 64 == 0))
     return launch_gemm_lds(X, xdtype, act_scale, packed, scales, zeros, M, N, K, bits, group_size, asymmetric, Y,

@@ -48,6 +48,11 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 128, kBN = 256, kBK = 64;
+
+// Strides between the entries of a batched launch (elements of each array).
+struct RegbBatch {
+  int64_t s_stride, packed_stride, sz_stride, y_stride;
+};
 constexpr int kThreads = 256;
 constexpr int kLD = kBK + 8;                          // A row pitch in halves (144 B: conflict-free ds_read_b128)
 constexpr int kStage = kBM * kLD;                     // halves per A stage
@@ -73,8 +78,18 @@ template <bool ASYM, bool SCALE, bool SZL>
 __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ s, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int M, int N, int K, int G,
-    uint16_t* __restrict__ Y, int tiles_m, int tiles_n) {
+    uint16_t* __restrict__ Y, int tiles_m, int tiles_n, RegbBatch bt) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+  // Batch entry blockIdx.y (one entry unless batched): its own scale vector,
+  // packed set and output over the same X.
+  {
+    const int64_t b = blockIdx.y;
+    if (SCALE) s += b * bt.s_stride;
+    packed += b * bt.packed_stride;
+    scales += b * bt.sz_stride;
+    if (ASYM) zeros += b * bt.sz_stride;
+    Y += b * bt.y_stride;
+  }
   __shared__ uint32_t szs[SZL ? kSZWords : 1];
 
   const int T = tiles_m * tiles_n;
@@ -288,22 +303,34 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
 
 template <bool ASYM, bool SCALE, bool SZL>
 hipError_t launch_sz(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
-                     int64_t M, int64_t N, int64_t K, int G, void* Y, hipStream_t stream) {
+                     int64_t M, int64_t N, int64_t K, int G, void* Y, int batch, RegbBatch bt, hipStream_t stream) {
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
   const int T = tiles_m * tiles_n;
+  // a multiple of 8, so that blockIdx.x % 8 is the XCD also in a batched grid
   const unsigned blocks = 8u * (unsigned)((T + 7) / 8);
-  hipLaunchKernelGGL((gemm_regb_kernel<ASYM, SCALE, SZL>), dim3(blocks), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((gemm_regb_kernel<ASYM, SCALE, SZL>), dim3(blocks, (unsigned)batch), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
                      static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N, (int)K,
-                     G, static_cast<uint16_t*>(Y), tiles_m, tiles_n);
+                     G, static_cast<uint16_t*>(Y), tiles_m, tiles_n, bt);
   return hipGetLastError();
 }
 
 template <bool ASYM, bool SCALE>
 hipError_t launch_one(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
-                      int64_t M, int64_t N, int64_t K, int G, void* Y, hipStream_t stream) {
-  return K / G <= kSZMaxGroups ? launch_sz<ASYM, SCALE, true>(X, s, packed, scales, zeros, M, N, K, G, Y, stream)
-                               : launch_sz<ASYM, SCALE, false>(X, s, packed, scales, zeros, M, N, K, G, Y, stream);
+                      int64_t M, int64_t N, int64_t K, int G, void* Y, int batch, RegbBatch bt, hipStream_t stream) {
+  return K / G <= kSZMaxGroups
+             ? launch_sz<ASYM, SCALE, true>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream)
+             : launch_sz<ASYM, SCALE, false>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream);
+}
+
+hipError_t launch_any(const void* X, const float* act_scale, const void* packed, const void* scales,
+                      const void* zeros, int64_t M, int64_t N, int64_t K, int G, bool asymmetric, void* Y, int batch,
+                      RegbBatch bt, hipStream_t stream) {
+  if (asymmetric)
+    return act_scale ? launch_one<true, true>(X, act_scale, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream)
+                     : launch_one<true, false>(X, act_scale, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream);
+  return act_scale ? launch_one<false, true>(X, act_scale, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream)
+                   : launch_one<false, false>(X, act_scale, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream);
 }
 
 }  // namespace
@@ -311,11 +338,16 @@ hipError_t launch_one(const void* X, const float* s, const void* packed, const v
 hipError_t launch_gemm_regb(const void* X, const float* act_scale, const void* packed, const void* scales,
                             const void* zeros, int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric,
                             void* Y, hipStream_t stream) {
-  if (asymmetric)
-    return act_scale ? launch_one<true, true>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream)
-                     : launch_one<true, false>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream);
-  return act_scale ? launch_one<false, true>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream)
-                   : launch_one<false, false>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream);
+  return launch_any(X, act_scale, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, 1, RegbBatch{0, 0, 0, 0},
+                    stream);
+}
+
+hipError_t launch_gemm_regb_batched(const void* X, const float* act_scale, int64_t s_stride, const void* packed,
+                                    int64_t packed_stride, const void* scales, const void* zeros, int64_t sz_stride,
+                                    int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric, void* Y,
+                                    int64_t y_stride, int batch, hipStream_t stream) {
+  return launch_any(X, act_scale, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, batch,
+                    RegbBatch{s_stride, packed_stride, sz_stride, y_stride}, stream);
 }
 
 }  // namespace woq

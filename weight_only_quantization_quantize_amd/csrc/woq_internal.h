@@ -24,6 +24,9 @@ hipError_t launch_gemm(const void* X, int xdtype, const float* act_scale, const 
                        const void* scales, const void* zeros, int64_t M, int64_t N, int64_t K, int bits,
                        int group_size, bool asymmetric, void* Y, hipStream_t stream);
 
+// Whether launch_gemm takes the register-B kernel for this shape.
+bool gemm_uses_regb(int64_t M, int64_t N, int64_t K, int bits, int xdtype);
+
 // Large-M GEMM: LDS-staged 256 x 256 tiles on 32x32x16 MFMA (bf16, 3-bit,
 // and fp16 shapes whose tiles fill the chip).
 hipError_t launch_gemm_lds(const void* X, int xdtype, const float* act_scale, const void* packed,
@@ -35,6 +38,14 @@ hipError_t launch_gemm_lds(const void* X, int xdtype, const float* act_scale, co
 hipError_t launch_gemm_regb(const void* X, const float* act_scale, const void* packed, const void* scales,
                             const void* zeros, int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric,
                             void* Y, hipStream_t stream);
+// The same for `batch` products over one X: entry b uses act_scale + b
+// s_stride, packed + b packed_stride (bytes), scales / zeros + b sz_stride
+// and writes Y + b y_stride (elements); one launch fills the chip where one
+// product's tiles would not.
+hipError_t launch_gemm_regb_batched(const void* X, const float* act_scale, int64_t s_stride, const void* packed,
+                                    int64_t packed_stride, const void* scales, const void* zeros, int64_t sz_stride,
+                                    int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric, void* Y,
+                                    int64_t y_stride, int batch, hipStream_t stream);
 
 // Small-batch GEMM (2 <= M <= 64, 4-bit, group 128, K = 2048 * {1, 2, 4}):
 // 16 X rows stay in registers while 16-column tiles of codes stream past.

@@ -494,6 +494,36 @@ def test_gemm_large_m_tiles(xdtype, bits, asym, G, K, awq):
     gemm_case(W, X, xdtype, bits, asym, G=G, s=s, label="large-M")
 
 
+@pytest.mark.parametrize("G,asym", [(256, True), (128, True), (64, False), (64, True)])
+def test_gemm_large_m_scale_staging(G, asym):
+    # fp16 register-B kernel with K / G a multiple of 8 (8, 16, 32 groups per
+    # row): each tile's scales and zero points are staged from 16-byte loads
+    # when both arrays are 16-byte aligned, and from 2-byte loads otherwise;
+    # N = 520 leaves 8 live columns in the last tile, whose staging chunks
+    # past the array end are clamped.  Both must give the same bits and match
+    # the oracle.
+    rng = np.random.default_rng(900 + G + int(asym))
+    M, N, K = 300, 520, 2048
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    err = gemm_case(W, X, "f16", 4, asym, G=G, label="scale-staging")
+    assert err <= REL_L2
+    packed, scales, zeros = ops.quantize_pack(gpu_f16(W), 4, G, asym)
+    Y16 = ops.gemm(gpu_f16(X), packed, scales, zeros, N, K, 4, G)
+    sbuf = torch.empty(scales.numel() + 1, dtype=torch.float16, device=DEV)
+    s_odd = sbuf[1:].view(scales.shape)
+    s_odd.copy_(scales)
+    z_odd = None
+    if asym:
+        zbuf = torch.empty(zeros.numel() + 1, dtype=torch.float16, device=DEV)
+        z_odd = zbuf[1:].view(zeros.shape)
+        z_odd.copy_(zeros)
+    assert scales.data_ptr() % 16 == 0 and s_odd.data_ptr() % 16 == 2
+    Y2 = ops.gemm(gpu_f16(X), packed, s_odd, z_odd, N, K, 4, G)
+    torch.cuda.synchronize()
+    assert torch.equal(Y16.view(torch.int16), Y2.view(torch.int16))
+
+
 @pytest.mark.parametrize("asym,awq", [(True, False), (False, True)])
 def test_gemm_large_m_full_chip_f16(asym, awq):
     # fp16, 4-bit: a 4096 x 4096 output is 256 tiles of 256 x 256, one round

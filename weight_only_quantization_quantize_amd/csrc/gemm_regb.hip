@@ -74,7 +74,12 @@ __device__ inline uint32_t dequant_pair(uint32_t magic_codes2, uint32_t zmagic2,
   return __builtin_bit_cast(uint32_t, d * __builtin_bit_cast(h2_t, s2));
 }
 
-template <bool ASYM, bool SCALE, bool SZL>
+// SZ: how the tile's scales and zero points reach the MFMA loop.
+//   0: one 2-byte load per lane and block (K / G above the LDS limit);
+//   1: staged in LDS once per tile with 2-byte loads;
+//   2: staged in LDS once per tile from 16-byte loads, every load issued
+//      before the first is waited for (arrays 16-byte aligned, K / G % 8 == 0).
+template <bool ASYM, bool SCALE, int SZ>
 __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ s, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int M, int N, int K, int G,
@@ -90,6 +95,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
     if (ASYM) zeros += b * bt.sz_stride;
     Y += b * bt.y_stride;
   }
+  constexpr bool SZL = SZ > 0;
   __shared__ uint32_t szs[SZL ? kSZWords : 1];
 
   const int T = tiles_m * tiles_n;
@@ -131,9 +137,29 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
 
   // SZL: the tile's scales and zero points, S | Z << 16 per (column, group)
   // with pitch gpr + 1 (conflict-free for 32 consecutive columns), loaded
-  // once with contiguous 2-byte loads; otherwise every block loads its own.
+  // once with contiguous loads; otherwise every block loads its own.  The
+  // 2-byte form waits for each load before the next (one memory latency per
+  // entry a thread stages); the 16-byte form has all of a thread's loads
+  // (at most 5 per array) in flight at once.
   const int szp = gpr + 1;
-  if constexpr (SZL) {
+  constexpr int kSZChunks = kBN * kSZMaxGroups / 8 / kThreads;  // 16-byte chunks per thread and array
+  u32x4_t szv_s[SZ == 2 ? kSZChunks : 1], szv_z[SZ == 2 ? kSZChunks : 1];
+  const int sz_chunks = kBN * gpr / 8;
+  if constexpr (SZ == 2) {
+    // The tile's slice of each [N, gpr] array is 256 gpr contiguous entries
+    // from entry n0 gpr; chunks past the array end (columns past N, never
+    // stored) read the last chunk.
+    const int64_t c0 = (int64_t)n0 * gpr / 8, clast = (int64_t)N * gpr / 8 - 1;
+#pragma unroll
+    for (int t = 0; t < kSZChunks; ++t) {
+      const int q = tid + kThreads * t;
+      int64_t ci = c0 + (q < sz_chunks ? q : sz_chunks - 1);
+      ci = ci < clast ? ci : clast;
+      szv_s[t] = reinterpret_cast<const u32x4_t*>(scales)[ci];
+      if (ASYM) szv_z[t] = reinterpret_cast<const u32x4_t*>(zeros)[ci];
+    }
+  }
+  if constexpr (SZ == 1) {
     const int total = kBN * gpr, q = kThreads / gpr, r = kThreads % gpr;
     int c = tid / gpr, g = tid % gpr;
     const int64_t row0 = (int64_t)n0 * gpr;
@@ -257,6 +283,24 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
   BRegs RB, RN;
   load_a(RA, 0);
   load_b(RB, 0);
+  if constexpr (SZ == 2) {
+    // chunk q holds entries 8q .. 8q + 7 of the slice: one column c, groups
+    // g .. g + 7 (gpr % 8 == 0)
+#pragma unroll
+    for (int t = 0; t < kSZChunks; ++t) {
+      const int q = tid + kThreads * t;
+      if (q < sz_chunks) {
+        const int e0 = 8 * q, c = e0 / gpr, g = e0 - c * gpr;
+        uint32_t* dst = szs + c * szp + g;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t sv = szv_s[t][e], zv = ASYM ? szv_z[t][e] : 0u;
+          dst[2 * e] = (sv & 0xFFFFu) | (zv << 16);
+          dst[2 * e + 1] = (sv >> 16) | (zv & 0xFFFF0000u);
+        }
+      }
+    }
+  }
   store_a(RA, 0, 0);
   __syncthreads();
   for (int kt = 0; kt < kblocks; ++kt) {
@@ -301,14 +345,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
   }
 }
 
-template <bool ASYM, bool SCALE, bool SZL>
+template <bool ASYM, bool SCALE, int SZ>
 hipError_t launch_sz(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
                      int64_t M, int64_t N, int64_t K, int G, void* Y, int batch, RegbBatch bt, hipStream_t stream) {
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
   const int T = tiles_m * tiles_n;
   // a multiple of 8, so that blockIdx.x % 8 is the XCD also in a batched grid
   const unsigned blocks = 8u * (unsigned)((T + 7) / 8);
-  hipLaunchKernelGGL((gemm_regb_kernel<ASYM, SCALE, SZL>), dim3(blocks, (unsigned)batch), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((gemm_regb_kernel<ASYM, SCALE, SZ>), dim3(blocks, (unsigned)batch), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
                      static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N, (int)K,
                      G, static_cast<uint16_t*>(Y), tiles_m, tiles_n, bt);
@@ -318,9 +362,14 @@ hipError_t launch_sz(const void* X, const float* s, const void* packed, const vo
 template <bool ASYM, bool SCALE>
 hipError_t launch_one(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
                       int64_t M, int64_t N, int64_t K, int G, void* Y, int batch, RegbBatch bt, hipStream_t stream) {
-  return K / G <= kSZMaxGroups
-             ? launch_sz<ASYM, SCALE, true>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream)
-             : launch_sz<ASYM, SCALE, false>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream);
+  const int64_t gpr = K / G;
+  if (gpr > kSZMaxGroups)
+    return launch_sz<ASYM, SCALE, 0>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream);
+  const bool aligned16 = (reinterpret_cast<uintptr_t>(scales) % 16 == 0) &&
+                         (!ASYM || reinterpret_cast<uintptr_t>(zeros) % 16 == 0) && bt.sz_stride % 8 == 0;
+  if (gpr % 8 == 0 && aligned16)
+    return launch_sz<ASYM, SCALE, 2>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream);
+  return launch_sz<ASYM, SCALE, 1>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream);
 }
 
 hipError_t launch_any(const void* X, const float* act_scale, const void* packed, const void* scales,

@@ -473,6 +473,45 @@ def test_gemm_skinny_one_hot_rows_and_guard(M):
         assert np.array_equal(Yh[m].view(np.uint16), w_hat16[:, k].view(np.uint16)), k
 
 
+# Mid M (33..127 rows of fp16 X, 4-bit codes, K % 64 == 0) takes
+# the mid-M kernel: 64 x 128 tiles whose K blocks are split between two
+# halves of the workgroup.  Ragged M and N tiles, an odd number of K blocks,
+# K / G = 64 (staged) and 128 (per-block loads), symmetric codes, AWQ scales;
+# at 33..64 rows only when N >= 16384 or the small-batch kernel cannot take
+# the shape (here K is not 4096 or 8192).
+@pytest.mark.parametrize("M,N,K,G,asym,awq", [
+    (33, 4200, 2048, 128, True, False), (64, 4096, 1088, 64, True, False),
+    (64, 4224, 2048, 32, False, False), (100, 4100, 4096, 32, True, False),
+    (127, 4160, 1536, 128, True, True), (48, 16400, 8192, 128, False, True)])
+def test_gemm_mid_m(M, N, K, G, asym, awq):
+    rng = np.random.default_rng(M * 7 + K + G)
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X32 = rng.standard_normal((M, K)).astype(np.float32)
+    s = None
+    if awq:
+        s = np.exp(rng.uniform(-1.0, 1.0, K)).astype(np.float32)
+        X32[:, rng.choice(K, 8, replace=False)] *= 20.0
+    rows = np.concatenate([np.sort(rng.choice(N - 8, 192, replace=False)), np.arange(N - 8, N)])
+    gemm_case(W, X32.astype(np.float16), "f16", 4, asym, G=G, s=s, rows=rows, label="mid-M")
+
+
+def test_gemm_mid_m_leaves_memory_past_y_untouched_and_repeats():
+    rng = np.random.default_rng(4040)
+    M, N, K = 40, 4100, 1088
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X = gpu_f16(rng.standard_normal((M, K)).astype(np.float16))
+    packed, scales, zeros = ops.quantize_pack(gpu_f16(W), 4, 64, True)
+    guard = 4096
+    buf = torch.full((M * N + 2 * guard,), 3.0, dtype=torch.float16, device=DEV)
+    Y = buf[guard: guard + M * N].view(M, N)
+    ops.gemm(X, packed, scales, zeros, N, K, 4, 64, out=Y)
+    first = Y.clone()
+    ops.gemm(X, packed, scales, zeros, N, K, 4, 64, out=Y)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:guard] == 3.0) and torch.all(buf[guard + M * N:] == 3.0)
+    assert torch.equal(first.view(torch.int16), Y.view(torch.int16))
+
+
 # Large M (>= 128) takes the LDS-staged MFMA kernel: ragged M and N tiles,
 # groups that do not divide its K block, AWQ scales, and for fp16 the
 # fallback to the direct kernel when K % 64 != 0.

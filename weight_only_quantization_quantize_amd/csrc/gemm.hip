@@ -478,15 +478,34 @@ bool gemm_uses_regb(int64_t M, int64_t N, int64_t K, int bits, int xdtype) {
   return M >= kLdsGemmMinM && xdtype == 0 && bits == 4 && K % 64 == 0 && !lds_tiles_fill_chip(M, N);
 }
 
+// The mid-M kernel (gemm_mid.hip, fp16 X, 4-bit codes, 64 x 128 tiles) takes
+// 33..127 rows: always above 64 rows (the small-batch kernel stops at 64 and
+// the direct kernel is 2.3x slower at 96..127 rows on K = 8192,
+// N = 28672), and at 33..64 rows when N gives it at least 128 tiles of
+// columns or the small-batch kernel cannot take the shape (measured at
+// M = 64, K = 8192: 56.5 against 72.3 us at N = 28672; at N = 11008,
+// K = 4096 the small-batch kernel is faster, 20.7 against 25.7 us).
+constexpr int64_t kMidMinM = 33;
+constexpr int64_t kMidMinN = 16384;
+
+bool gemm_uses_mid(int64_t M, int64_t N, int64_t K, int bits, int xdtype, bool skinny_ok) {
+  return M >= kMidMinM && M < kLdsGemmMinM && xdtype == 0 && bits == 4 && K % 64 == 0 &&
+         (M > 64 || N >= kMidMinN || !skinny_ok);
+}
+
 hipError_t launch_gemm(const void* X, int xdtype, const float* act_scale, const void* packed, const void* scales,
                        const void* zeros, int64_t M, int64_t N, int64_t K, int bits, int group_size, bool asymmetric,
                        void* Y, hipStream_t stream) {
   if (gemm_uses_regb(M, N, K, bits, xdtype))
     return launch_gemm_regb(X, act_scale, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, stream);
+  const bool skinny_ok =
+      gemm_skinny_supported(M, N, K, xdtype, act_scale != nullptr, bits, group_size, scales, zeros);
+  if (gemm_uses_mid(M, N, K, bits, xdtype, skinny_ok))
+    return launch_gemm_mid(X, act_scale, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, stream);
   if (M >= kLdsGemmMinM && (xdtype != 0 || K % 64 == 0))
     return launch_gemm_lds(X, xdtype, act_scale, packed, scales, zeros, M, N, K, bits, group_size, asymmetric, Y,
                            stream);
-  if (gemm_skinny_supported(M, N, K, xdtype, act_scale != nullptr, bits, group_size, scales, zeros))
+  if (skinny_ok)
     return launch_gemm_skinny(X, xdtype, act_scale, packed, scales, zeros, M, N, K, asymmetric, Y, stream);
   if (bits == 4)
     return asymmetric

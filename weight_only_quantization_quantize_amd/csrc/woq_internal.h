@@ -42,6 +42,12 @@ hipError_t launch_gemm_regb(const void* X, const float* act_scale, const void* p
 // s_stride, packed + b packed_stride (bytes), scales / zeros + b sz_stride
 // and writes Y + b y_stride (elements); one launch fills the chip where one
 // product's tiles would not.
+// Mid-M GEMM (fp16 X, 4-bit codes, K % 64 == 0): 64 x 128 tiles, K split
+// between two halves of the workgroup that meet in LDS.
+hipError_t launch_gemm_mid(const void* X, const float* act_scale, const void* packed, const void* scales,
+                           const void* zeros, int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric,
+                           void* Y, hipStream_t stream);
+bool gemm_uses_mid(int64_t M, int64_t N, int64_t K, int bits, int xdtype, bool skinny_ok);
 hipError_t launch_gemm_regb_batched(const void* X, const float* act_scale, int64_t s_stride, const void* packed,
                                     int64_t packed_stride, const void* scales, const void* zeros, int64_t sz_stride,
                                     int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric, void* Y,

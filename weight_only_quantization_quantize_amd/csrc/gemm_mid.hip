@@ -51,7 +51,6 @@ constexpr int kAUnits = kBM * kASegs / kHalf;         // A segments per thread
 constexpr int kARowStep = kHalf / kASegs;             // rows between a thread's segments
 constexpr int kSZMaxGroups = 64;                      // K / G up to which S and Z are staged in LDS
 constexpr int kSZWords = kBN * (kSZMaxGroups + 1);    // S | Z << 16 per (column, group), odd pitch
-constexpr int kRing = 3;                              // K steps of loads in flight
 
 __device__ inline float16_t mfma32(u32x4_t a, u32x4_t b, float16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c, 0,
@@ -67,8 +66,11 @@ __device__ inline uint32_t dequant_pair(uint32_t magic_codes2, uint32_t zmagic2,
 
 // SZ: 0 = one 2-byte S / Z load per lane and block (K / G > 64); 1 = staged
 // in LDS with 2-byte loads; 2 = staged from 16-byte loads.
-template <bool ASYM, bool SCALE, int SZ>
-__global__ __launch_bounds__(kThreads, 2) void gemm_mid_kernel(const uint16_t* __restrict__ X,
+// kRing: K steps of loads in flight.  4 for a single row of tiles (M <= 64:
+// one workgroup per compute unit at most, so the ring's registers cost no
+// occupancy), 3 otherwise (two workgroups per compute unit).
+template <bool ASYM, bool SCALE, int SZ, int kRing>
+__global__ __launch_bounds__(kThreads, kRing == 3 ? 2 : 1) void gemm_mid_kernel(const uint16_t* __restrict__ X,
                                                                const float* __restrict__ s,
                                                                const uint8_t* __restrict__ packed,
                                                                const uint16_t* __restrict__ scales,
@@ -317,10 +319,16 @@ hipError_t launch_sz(const void* X, const float* s, const void* packed, const vo
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
   const int T = tiles_m * tiles_n;
   const unsigned blocks = 8u * (unsigned)((T + 7) / 8);  // blockIdx.x % 8 is the XCD
-  hipLaunchKernelGGL((gemm_mid_kernel<ASYM, SCALE, SZ>), dim3(blocks), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
-                     static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N, (int)K,
-                     G, static_cast<uint16_t*>(Y), tiles_m, tiles_n);
+  if (tiles_m == 1)
+    hipLaunchKernelGGL((gemm_mid_kernel<ASYM, SCALE, SZ, 4>), dim3(blocks), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
+                       static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N,
+                       (int)K, G, static_cast<uint16_t*>(Y), tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_mid_kernel<ASYM, SCALE, SZ, 3>), dim3(blocks), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
+                       static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N,
+                       (int)K, G, static_cast<uint16_t*>(Y), tiles_m, tiles_n);
   return hipGetLastError();
 }
 

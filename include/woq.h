@@ -134,12 +134,14 @@ woq_status woq_w4a16_gemv(const void* x, int32_t xdtype, const float* act_scale,
  *   X : [M, K] row-major of xdtype;  Y : out, [M, N] row-major of xdtype.
  * Small M decodes weights in registers and feeds MFMA with an exact integer
  * (u - Z) and per-group fp32 scaling.  Large M (M >= 128 and, for fp16,
- * K % 64 == 0) feeds MFMA with dequantized weights: for fp16, w_hat rounded
- * once to fp16 (decoded straight into operand registers for 4-bit codes, or
- * staged in LDS) with X * fl32(1 / s) rounded once to fp16; for bf16, X used
- * as given and w_hat * fl32(1 / s) kept as a bf16 pair hi + lo (about 16
- * significant bits).  fp32 accumulation throughout; the order of the K sum
- * inside an MFMA step is the kernel's. */
+ * K % 64 == 0), and fp16 X with 4-bit codes and K % 64 == 0 at 33..127 rows
+ * (always above 64 rows; at 33..64 rows when N >= 16384 or the small-batch
+ * kernel does not take the shape), feed MFMA with dequantized weights: for
+ * fp16, w_hat rounded once to fp16 (decoded straight into operand registers
+ * for 4-bit codes, or staged in LDS) with X * fl32(1 / s) rounded once to
+ * fp16; for bf16, X used as given and w_hat * fl32(1 / s) kept as a bf16 pair
+ * hi + lo (about 16 significant bits).  fp32 accumulation throughout; the
+ * order of the K sum inside an MFMA step is the kernel's. */
 woq_status woq_w4a16_gemm(const void* X, int32_t xdtype, const float* act_scale,
                           const void* packed, const void* scales, const void* zeros,
                           int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size,

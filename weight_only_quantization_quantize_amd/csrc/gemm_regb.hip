@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
     Y += b * bt.y_stride;
   }
   constexpr bool SZL = SZ > 0;
-  __shared__ uint32_t szs[SZL ? kSZWords : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t szs[SZL ? kSZWords : 1];
 
   const int T = tiles_m * tiles_n;
   const int per_xcd = (T + 7) / 8;
@@ -316,8 +316,40 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
     __syncthreads();
   }
 
-  // Epilogue: for accumulator (i, j, v) the 32 lanes of each half-wave hold
-  // 32 consecutive columns of one row.
+  // Epilogue, full tiles with N % 8 == 0 and the scales staged in LDS (both
+  // LDS arrays are free after the loop's last barrier): each wave writes its
+  // 128 x 64 fp16 block into a region of its own (pitch 72 halves) and stores
+  // it back as 16-byte row segments, 16 stores per lane instead of 128.  The
+  // region is the wave's alone and a wave's LDS operations complete in
+  // order, so a wavefront-scope fence stands in for a barrier.
+  if constexpr (SZL) {
+    if (m0 + kBM <= M && n0 + kBN <= N && N % 8 == 0) {
+      constexpr int kOP = 72;
+      uint16_t* region = wave < 2 ? lds + wave * (kBM * kOP)
+                                  : reinterpret_cast<uint16_t*>(szs) + (wave - 2) * (kBM * kOP);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            region[(32 * i + 8 * (v >> 2) + 4 * fh + (v & 3)) * kOP + 32 * j + fr] = F16::from_f32(acc[i][j][v]);
+      // the lanes of this wave read what other lanes wrote: keep the reads
+      // after the writes (a wavefront-scope fence; LDS order does the rest)
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const int ch = lane & 7;
+      uint16_t* __restrict__ ybase = Y + (int64_t)m0 * N + n0 + 64 * wave + 8 * ch;
+#pragma unroll
+      for (int it = 0; it < kBM / 8; ++it) {
+        const int row = 8 * it + (lane >> 3);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(region + row * kOP + 8 * ch);
+        *reinterpret_cast<u32x4_t*>(ybase + (int64_t)row * N) = v;
+      }
+      return;
+    }
+  }
+  // Otherwise: for accumulator (i, j, v) the 32 lanes of each half-wave hold
+  // 32 consecutive columns of one row; one 2-byte store per output.
   const int row_base = m0 + 4 * fh;
   const int col_base = n0 + 64 * wave + fr;
   uint16_t* __restrict__ yb = Y + (int64_t)row_base * N + col_base;

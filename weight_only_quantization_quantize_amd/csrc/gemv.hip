@@ -16,8 +16,9 @@
 //
 // Order of the stream.  Workgroup b handles the row groups b, b + B, b + 2B,
 // ... (B = number of workgroups), so at every step the whole GPU reads one
-// contiguous window of B * RPB rows; each wave keeps kPrefetch steps of code
-// loads in flight ahead of the step it computes.
+// contiguous window of B * RPB rows; each wave keeps 2 steps of code loads
+// in flight ahead of the step it computes (4 on the general path with 8 row
+// steps per workgroup).
 //
 // Decode.  fp16 activations: a masked 4-bit code pair (w & 0x000F000F, or
 // w & 0x00F000F0 for the pair one nibble up) is read by v_dot2 as two fp16
@@ -213,6 +214,11 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
   const int row_first = (int)blockIdx.x * rpb + rr;
   const int row_step = (int)gridDim.x * rpb;
 
+  // Steps of code loads in flight: twice as many on the general path with 8
+  // row steps per workgroup (few waves per compute unit there; e.g. K = 11008,
+  // N = 4096: 10.60 -> 10.19 us), kPrefetch elsewhere (4 slowed the
+  // fixed-shape K = N = 8192 launch, 8.30 -> 8.50 us).
+  constexpr int kPf = (!kFixed && STEPS >= 8) ? 2 * kPrefetch : kPrefetch;
   StepLoads<BITS> L[STEPS];
   auto issue = [&](int st) {
     int n = row_first + st * row_step;
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
     }
   }
 #pragma unroll
-  for (int st = 0; st < kPrefetch && st < STEPS; ++st) issue(st);
+  for (int st = 0; st < kPf && st < STEPS; ++st) issue(st);
 
   // Stage x' = x / s, rounded once to the activation type, in LDS.
 #pragma unroll
@@ -291,7 +297,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
   const float zsym = (float)(1 << (BITS - 1));
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
-    if (st + kPrefetch < STEPS) issue(st + kPrefetch);
+    if (st + kPf < STEPS) issue(st + kPf);
     const float S = half_bits_to_f32(L[st].s16);
     const float Z = ASYM ? half_bits_to_f32(L[st].z16) : zsym;
     float d = chunk_dot<BITS, XT>(L[st].c, xr, xs, Z, magic);

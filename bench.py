@@ -33,6 +33,8 @@ after all timing, and never with --no-cpu-baseline.
 `--write-traffic DIR` turns the rocprofv3 FETCH_SIZE / WRITE_SIZE CSVs of a
 bench run and of a `--copy-calibration` run (pmc_fetch, pmc_write,
 pmc_copy_fetch, pmc_copy_write under DIR) into profiles/gemv_traffic.json.
+`--gemm-only M,N,K` runs five GEMMs of one shape and nothing else, for
+rocprofv3 counter runs of a single GEMM kernel.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--variants] [--no-rows]
 """
@@ -83,6 +85,9 @@ def parse():
     p.add_argument("--copy-mib", type=int, default=256, help="size of the --copy-calibration run used for DIR")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (for HBM counter calibration) and exit")
+    p.add_argument("--gemm-only", default=None, metavar="M,N,K",
+                   help="only run five fp16 4-bit asymmetric g128 GEMMs of this shape on seeded inputs "
+                        "(for rocprofv3 counter runs) and exit")
     return p.parse_args()
 
 
@@ -523,6 +528,19 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
+    if args.gemm_only:
+        # W ~ N(0, 0.02), X ~ N(0, 1), drawn on the device from fixed seeds
+        M, N, K = (int(v) for v in args.gemm_only.split(","))
+        g = torch.Generator(device=dev).manual_seed(7000)
+        W = (torch.randn(N, K, generator=g, device=dev) * 0.02).to(torch.float16)
+        X = torch.randn(M, K, generator=g, device=dev).to(torch.float16)
+        packed, scales, zeros = ops.quantize_pack(W, 4, 128, True)
+        Y = torch.empty(M, N, dtype=torch.float16, device=dev)
+        for _ in range(5):
+            ops.gemm(X, packed, scales, zeros, N, K, 4, 128, out=Y)
+        torch.cuda.synchronize()
+        print(json.dumps({"gemm_only": [M, N, K], "launches": 5}), flush=True)
         return
     _lib.load()
     torch.cuda.set_device(dev)

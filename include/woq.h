@@ -140,7 +140,9 @@ woq_status woq_w4a16_gemv(const void* x, int32_t xdtype, const float* act_scale,
  * fp16, w_hat rounded once to fp16 (decoded straight into operand registers
  * for 4-bit codes, or staged in LDS) with X * fl32(1 / s) rounded once to
  * fp16; for bf16, X used as given and w_hat * fl32(1 / s) kept as a bf16 pair
- * hi + lo (about 16 significant bits).  fp32 accumulation throughout; the
+ * hi + lo (about 16 significant bits), or, for bf16 X at 33..127 rows without
+ * an AWQ scale (group size a power of two >= 64), the exact 128 + u with the
+ * scale applied per group in fp32.  fp32 accumulation throughout; the
  * order of the K sum inside an MFMA step is the kernel's. */
 woq_status woq_w4a16_gemm(const void* X, int32_t xdtype, const float* act_scale,
                           const void* packed, const void* scales, const void* zeros,

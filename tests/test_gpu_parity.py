@@ -495,14 +495,33 @@ def test_gemm_mid_m(M, N, K, G, asym, awq):
     gemm_case(W, X32.astype(np.float16), "f16", 4, asym, G=G, s=s, rows=rows, label="mid-M")
 
 
-def test_gemm_mid_m_leaves_memory_past_y_untouched_and_repeats():
+# bf16 X with 4-bit codes at 33..127 rows takes the bf16 mid-M kernel (G a
+# power of two >= 64, no AWQ scale): weights kept exact as 128 + u, the scale
+# applied per group in fp32.  An odd number of K blocks, a group split between
+# the two K halves (K = 1152, G = 128), G = 64 / 128 / 256, symmetric codes.
+@pytest.mark.parametrize("M,N,K,G,asym", [
+    (33, 4200, 2048, 128, True), (64, 16400, 8192, 128, True), (100, 4100, 4096, 64, True),
+    (127, 4160, 1536, 256, False), (48, 4096, 1088, 64, True), (40, 4100, 1152, 128, True)])
+def test_gemm_mid_m_bf16(M, N, K, G, asym):
+    rng = np.random.default_rng(M * 11 + K + G)
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X32 = rng.standard_normal((M, K)).astype(np.float32)
+    X32[:, rng.choice(K, 8, replace=False)] *= 20.0
+    rows = np.concatenate([np.sort(rng.choice(N - 8, 192, replace=False)), np.arange(N - 8, N)])
+    gemm_case(W, synth.to_bf16_bits(X32), "bf16", 4, asym, G=G, rows=rows, label="mid-M bf16")
+
+
+@pytest.mark.parametrize("xdtype", ["f16", "bf16"])
+def test_gemm_mid_m_leaves_memory_past_y_untouched_and_repeats(xdtype):
     rng = np.random.default_rng(4040)
     M, N, K = 40, 4100, 1088
     W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
-    X = gpu_f16(rng.standard_normal((M, K)).astype(np.float16))
+    X32 = rng.standard_normal((M, K)).astype(np.float32)
+    X = gpu_x(X32.astype(np.float16) if xdtype == "f16" else synth.to_bf16_bits(X32), xdtype)
     packed, scales, zeros = ops.quantize_pack(gpu_f16(W), 4, 64, True)
     guard = 4096
-    buf = torch.full((M * N + 2 * guard,), 3.0, dtype=torch.float16, device=DEV)
+    dt = torch.float16 if xdtype == "f16" else torch.bfloat16
+    buf = torch.full((M * N + 2 * guard,), 3.0, dtype=dt, device=DEV)
     Y = buf[guard: guard + M * N].view(M, N)
     ops.gemm(X, packed, scales, zeros, N, K, 4, 64, out=Y)
     first = Y.clone()

@@ -18,7 +18,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwoq.so")
 ARCH = os.environ.get("WOQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["woq_api.cpp", "quantize_pack.hip", "gemv.hip", "gemm.hip", "gemm_lds.hip", "gemm_regb.hip", "gemm_mid.hip", "gemm_skinny.hip", "dequantize.hip",
+SOURCES = ["woq_api.cpp", "quantize_pack.hip", "gemv.hip", "gemm.hip", "gemm_lds.hip", "gemm_regb.hip", "gemm_mid.hip", "gemm_mid_bf16.hip", "gemm_skinny.hip", "dequantize.hip",
            "awq_search.hip", "gptq.hip"]
 
 COMMON_FLAGS = [

@@ -502,6 +502,11 @@ hipError_t launch_gemm(const void* X, int xdtype, const float* act_scale, const 
       gemm_skinny_supported(M, N, K, xdtype, act_scale != nullptr, bits, group_size, scales, zeros);
   if (gemm_uses_mid(M, N, K, bits, xdtype, skinny_ok))
     return launch_gemm_mid(X, act_scale, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, stream);
+  // bf16 X: the same rows and widths, for group sizes the bf16 mid-M kernel
+  // takes and without an AWQ scale.
+  if (M >= kMidMinM && M < kLdsGemmMinM && xdtype == 1 && bits == 4 && act_scale == nullptr &&
+      gemm_mid_bf16_supported(K, group_size) && (M > 64 || N >= kMidMinN || !skinny_ok))
+    return launch_gemm_mid_bf16(X, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, stream);
   if (M >= kLdsGemmMinM && (xdtype != 0 || K % 64 == 0))
     return launch_gemm_lds(X, xdtype, act_scale, packed, scales, zeros, M, N, K, bits, group_size, asymmetric, Y,
                            stream);

@@ -48,6 +48,12 @@ hipError_t launch_gemm_mid(const void* X, const float* act_scale, const void* pa
                            const void* zeros, int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric,
                            void* Y, hipStream_t stream);
 bool gemm_uses_mid(int64_t M, int64_t N, int64_t K, int bits, int xdtype, bool skinny_ok);
+// Mid-M GEMM for bf16 X and 4-bit codes (K % 64 == 0, G a power of two >= 64,
+// no AWQ scale): the same tiles with the weights kept exact as 128 + u and the
+// scale applied per group in fp32.
+bool gemm_mid_bf16_supported(int64_t K, int group_size);
+hipError_t launch_gemm_mid_bf16(const void* X, const void* packed, const void* scales, const void* zeros, int64_t M,
+                                int64_t N, int64_t K, int group_size, bool asymmetric, void* Y, hipStream_t stream);
 hipError_t launch_gemm_regb_batched(const void* X, const float* act_scale, int64_t s_stride, const void* packed,
                                     int64_t packed_stride, const void* scales, const void* zeros, int64_t sz_stride,
                                     int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric, void* Y,

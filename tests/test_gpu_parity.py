@@ -498,10 +498,12 @@ def test_gemm_mid_m(M, N, K, G, asym, awq):
 # bf16 X with 4-bit codes at 33..127 rows takes the bf16 mid-M kernel (G a
 # power of two >= 64, no AWQ scale): weights kept exact as 128 + u, the scale
 # applied per group in fp32.  An odd number of K blocks, a group split between
-# the two K halves (K = 1152, G = 128), G = 64 / 128 / 256, symmetric codes.
+# the two K halves (K = 1152, G = 128), G = 64 / 128 / 256, K / G = 6 (2-byte
+# staging), 32 (16-byte staging) and 128 (per-block loads), symmetric codes.
 @pytest.mark.parametrize("M,N,K,G,asym", [
     (33, 4200, 2048, 128, True), (64, 16400, 8192, 128, True), (100, 4100, 4096, 64, True),
-    (127, 4160, 1536, 256, False), (48, 4096, 1088, 64, True), (40, 4100, 1152, 128, True)])
+    (127, 4160, 1536, 256, False), (48, 4096, 1088, 64, True), (40, 4100, 1152, 128, True),
+    (64, 16400, 8192, 64, True)])
 def test_gemm_mid_m_bf16(M, N, K, G, asym):
     rng = np.random.default_rng(M * 11 + K + G)
     W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)

@@ -263,11 +263,14 @@ def test_gptq_workspace_size(lib):
     assert lib.woq_gptq_workspace_bytes(T, N, K, 4, 96) == 0
 
 
-def test_gptq_symmetric_ignores_zeros(lib):
-    # zeros may be NULL for the symmetric form: validation passes and the call
-    # reaches the short-workspace check
+def test_gptq_symmetric_takes_no_zeros(lib):
+    # the symmetric form takes zeros = NULL: validation passes and the call
+    # reaches the short-workspace check; a non-NULL zeros is rejected, as for
+    # every other entry point
     assert _gptq(lib, asym=0, zeros=None, wsb=16) == _lib.WOQ_ERR_INVALID_ARGUMENT
     assert "workspace too small" in lib.woq_last_error().decode()
+    assert _gptq(lib, asym=0, zeros=FAKE) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    assert "zeros must be NULL when symmetric" in lib.woq_last_error().decode()
 
 
 def test_oversized_shapes_are_unsupported(lib):

@@ -2,7 +2,9 @@
 
 Packed codes, scales and zeros must match the oracle byte for byte; GEMV /
 GEMM outputs must be within relative L2 2e-3 of the oracle's fp64 result on
-the same dequantized weights.  Shapes span several tiles with ragged tails;
+the same dequantized weights, and every output element within the rounding
+bound of ``tests/parity_bound.py`` (input roundings, fp32 accumulation and the
+output type's rounding).  Shapes span several tiles with ragged tails;
 the full-size workloads are checked on sampled rows / columns that the
 oracle computes one by one.
 """
@@ -11,6 +13,7 @@ import pytest
 import torch
 
 from oracle import woq_oracle as O
+from tests.parity_bound import check_elementwise, output_bound
 from weight_only_quantization_quantize_amd import ops, synth
 
 pytestmark = pytest.mark.gpu
@@ -41,6 +44,21 @@ def host(t):
     if t.dtype == torch.bfloat16:
         return O.bf16_bits_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
     return t.cpu().numpy()
+
+
+def assert_output_close(y, y_ref, X64, q, s, out_dtype, label):
+    """Relative L2 over the whole output and the per-element rounding bound.
+    y, y_ref: [M, N'] (host fp64, oracle fp64); X64: exact activations
+    [M, K]; q: the oracle's Quantized of the N' rows compared."""
+    y = np.atleast_2d(np.asarray(y, dtype=np.float64))
+    y_ref = np.atleast_2d(y_ref)
+    err = O.rel_l2(y, y_ref)
+    bound = output_bound(X64, O.dequantize(q), q.scales, q.bits, q.group_size, s, y_ref, out_dtype)
+    ok, worst, where = check_elementwise(y, y_ref, bound)
+    _say(f"{label}: rel_l2={err:.2e} worst element {worst:.3f} of its bound at {where}")
+    assert err <= REL_L2, f"{label}: rel_l2 {err:.3e}"
+    assert ok, f"{label}: element {where} off by {worst:.2f}x its bound"
+    return err
 
 
 def quantize_both(W, bits, G, asym, s=None):
@@ -212,11 +230,10 @@ def gemv_case(lin, bits, asym, xdtype="f16", G=128, use_scale=True):
     assert_pack_equal(gpu, ref)
     X = lin.X if xdtype == "f16" else synth.to_bf16_bits(lin.X.astype(np.float32))
     y = ops.gemv(gpu_x(X[0], xdtype), *gpu, lin.N, lin.K, bits, G, gpu_f32(s))
-    y_ref = O.gemm(O.activations_f64(X, xdtype), O.dequantize(ref[3]), s)[0]
-    err = O.rel_l2(host(y), y_ref)
-    _say(f"gemv {lin.name} bits={bits} asym={asym} {xdtype} G={G}: rel_l2={err:.2e}")
-    assert err <= REL_L2
-    return err
+    X64 = O.activations_f64(X[:1], xdtype)
+    y_ref = O.gemm(X64, O.dequantize(ref[3]), s)
+    return assert_output_close(host(y)[None, :], y_ref, X64, ref[3], s, xdtype,
+                               f"gemv {lin.name} bits={bits} asym={asym} {xdtype} G={G}")
 
 
 @pytest.mark.parametrize("bits", [3, 4])
@@ -268,10 +285,10 @@ def test_fused_projection_gemv(which, bits, asym):
         assert np.array_equal(y.cpu().numpy().view(np.uint16), y_sep.cpu().numpy().view(np.uint16))
     W_all = np.concatenate([l.W for l in lins])
     _, _, _, q = O.quantize_pack(W_all, bits, 128, asym, s)
-    y_ref = O.gemm(O.activations_f64(x[None, :], "f16"), O.dequantize(q), s)[0]
-    err = O.rel_l2(np.concatenate([y.cpu().numpy() for y in ys]).astype(np.float64), y_ref)
-    _say(f"fused {which} N={sum(sizes)} K={K} bits={bits} asym={asym}: rel_l2={err:.2e}")
-    assert err <= REL_L2
+    X64 = O.activations_f64(x[None, :], "f16")
+    y_ref = O.gemm(X64, O.dequantize(q), s)
+    assert_output_close(np.concatenate([y.cpu().numpy() for y in ys])[None, :], y_ref, X64, q, s, "f16",
+                        f"fused {which} N={sum(sizes)} K={K} bits={bits} asym={asym}")
 
 
 @pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (67, 160), (129, 640), (33, 2048 + 128), (250, 8192 + 512),
@@ -331,11 +348,14 @@ def gemm_case(W, X, xdtype, bits, asym, G=128, s=None, rows=None, label=""):
     torch.cuda.synchronize()
     assert np.array_equal(packed.cpu().numpy()[sel], ref_packed)
     assert np.array_equal(scales.cpu().numpy()[sel].view(np.uint16), ref_scales.view(np.uint16))
-    Y_ref = O.gemm(O.activations_f64(X, xdtype), O.dequantize(q), s)
-    err = O.rel_l2(Yh[:, sel], Y_ref)
-    _say(f"gemm {label} M={M} N={N} K={K} bits={bits} asym={asym} {xdtype} G={G}: rel_l2={err:.2e}")
-    assert err <= REL_L2
-    return err
+    if asym:
+        assert np.array_equal(zeros.cpu().numpy()[sel].view(np.uint16), ref_zeros.view(np.uint16))
+    else:
+        assert zeros is None and ref_zeros is None
+    X64 = O.activations_f64(X, xdtype)
+    Y_ref = O.gemm(X64, O.dequantize(q), s)
+    return assert_output_close(Yh[:, sel], Y_ref, X64, q, s, xdtype,
+                               f"gemm {label} M={M} N={N} K={K} bits={bits} asym={asym} {xdtype} G={G}")
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 15, 16, 17, 33, 64, 65, 130])
@@ -440,8 +460,8 @@ def test_gemm_small_batch_with_2_byte_aligned_scales():
     Y = ops.gemm(gpu_f16(X), packed, s_odd, z_odd, N, K, 4, 128)
     Y_ref = ops.gemm(gpu_f16(X), packed, scales, zeros, N, K, 4, 128)
     q = O.quantize(W, 4, 128, True)
-    err = O.rel_l2(host(Y), O.gemm(X.astype(np.float64), O.dequantize(q)))
-    assert err <= REL_L2
+    X64 = X.astype(np.float64)
+    assert_output_close(host(Y), O.gemm(X64, O.dequantize(q)), X64, q, None, "f16", "gemm 2-byte aligned scales")
     assert O.rel_l2(host(Y), host(Y_ref).astype(np.float64)) <= REL_L2
 
 
@@ -765,8 +785,8 @@ def test_gptq_matches_oracle(T, N, K, bits, asym, G):
     # the result is consumable by the GEMV as any quantize_pack output
     x = synth.activations(1, K, seed + 4)
     y = ops.gemv(gpu_f16(x), packed, scales, zeros, N, K, bits, G)
-    y_ref = O.gemm(x.astype(np.float64), O.dequantize(q))
-    assert O.rel_l2(host(y)[None, :], y_ref) < REL_L2
+    X64 = x.astype(np.float64)
+    assert_output_close(host(y)[None, :], O.gemm(X64, O.dequantize(q)), X64, q, None, "f16", "gemv of gptq output")
 
 
 def test_gptq_llama_q_proj_sampled_rows():

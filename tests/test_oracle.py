@@ -569,3 +569,204 @@ def test_codes_with_params_matches_quantize():
             u = O.codes_with_params(W[:, k].astype(np.float32), q.scales[:, 0], None if q.zeros is None else q.zeros[:, 0],
                                     bits, asym)
             assert np.array_equal(u, q.codes[:, k])
+
+
+# ---------------------------------------------------------------------------
+# GPTQ worked in exact rational arithmetic on a tiny layer ("CMU 11-868
+# L19-L20", section "The algorithm in four steps").  The factor is never
+# formed: with A = (2 X^T X + lambda I)^-1 = Lt D Lt^T (Lt unit lower
+# triangular, D diagonal), the Cholesky factor is L = Lt D^(1/2), so the
+# update ratio U[k, j] / U[k, k] of the column step is exactly Lt[j, k], a
+# rational number.  Every rounding decision is replayed by exact rounding to
+# binary32 / binary16.  The case is chosen so that taking a group's
+# parameters from the original weights instead of the updated ones changes
+# the scales and the codes.
+# ---------------------------------------------------------------------------
+
+def _round_binary(v: Fraction, sig_bits: int, emin: int) -> Fraction:
+    """v rounded to the nearest binary float with sig_bits significant bits
+    (half to even), subnormals below 2^emin."""
+    if v == 0:
+        return Fraction(0)
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, emin) - (sig_bits - 1))
+    r = round(a / ulp) * ulp
+    return r if v > 0 else -r
+
+
+def _fl32(v):
+    return _round_binary(v, 24, -126)
+
+
+def _f16r(v):
+    return _round_binary(v, 11, -14)
+
+
+def _rtn_params_exact(vals, bits, asym):
+    vals = [_fl32(v) for v in vals]
+    if asym:
+        qu = 2 ** bits - 1
+        r = _fl32(max(vals) - min(vals))
+        S = _f16r(_fl32((r if r != 0 else Fraction(1)) / qu))
+        Z = min(max(round(_fl32(-min(vals) / S)), 0), qu) if S != 0 else 0
+        return S, Fraction(Z)
+    h = 2 ** (bits - 1)
+    return _f16r(_fl32(max(abs(v) for v in vals) / (h - 1))), Fraction(h)
+
+
+def _code_exact(v, S, Z, bits, asym):
+    q = round(_fl32(_fl32(v) / S))
+    if asym:
+        return min(max(q + int(Z), 0), 2 ** bits - 1)
+    h = 2 ** (bits - 1)
+    return min(max(q, -h), h - 1) + h
+
+
+def _inverse_exact(A):
+    n = len(A)
+    M = [list(r) + [Fraction(int(i == j)) for j in range(n)] for i, r in enumerate(A)]
+    for c in range(n):
+        p = next(r for r in range(c, n) if M[r][c] != 0)
+        M[c], M[p] = M[p], M[c]
+        M[c] = [v / M[c][c] for v in M[c]]
+        for r in range(n):
+            if r != c and M[r][c] != 0:
+                f = M[r][c]
+                M[r] = [a - f * b for a, b in zip(M[r], M[c])]
+    return [r[n:] for r in M]
+
+
+def _unit_lower_of_ldl(A):
+    n = len(A)
+    L = [[Fraction(int(i == j)) for j in range(n)] for i in range(n)]
+    D = [Fraction(0)] * n
+    for j in range(n):
+        D[j] = A[j][j] - sum(L[j][k] ** 2 * D[k] for k in range(j))
+        for i in range(j + 1, n):
+            L[i][j] = (A[i][j] - sum(L[i][k] * L[j][k] * D[k] for k in range(j))) / D[j]
+    return L
+
+
+def _gptq_exact(X, W, bits, G, asym, params_from_original=False):
+    T, K, N = len(X), len(X[0]), len(W)
+    H = [[2 * sum(X[t][i] * X[t][j] for t in range(T)) for j in range(K)] for i in range(K)]
+    lam = Fraction(1, 100) * sum(H[i][i] for i in range(K)) / K
+    for i in range(K):
+        H[i][i] += lam
+    Lt = _unit_lower_of_ldl(_inverse_exact(H))
+    w = [list(r) for r in W]
+    codes = [[0] * K for _ in range(N)]
+    S = [[None] * (K // G) for _ in range(N)]
+    Z = [[None] * (K // G) for _ in range(N)]
+    for k in range(K):
+        g = k // G
+        for n in range(N):
+            if k % G == 0:
+                src = W[n] if params_from_original else w[n]
+                S[n][g], Z[n][g] = _rtn_params_exact(src[k:k + G], bits, asym)
+            u = _code_exact(w[n][k], S[n][g], Z[n][g], bits, asym)
+            codes[n][k] = u
+            e = w[n][k] - (u - Z[n][g]) * S[n][g]
+            for j in range(k + 1, K):
+                w[n][j] -= e * Lt[j][k]
+    return codes, S, Z
+
+
+_GPTQ_TINY_X = [[-1.0, 1.5, 1.0, -2.0], [-0.5, 1.5, 0.0, -2.0], [1.0, 1.0, 1.5, -1.5]]
+_GPTQ_TINY_W = [[-0.875, 0.75, -1.0, 0.0625], [-0.875, -0.4375, -0.0625, -0.1875]]
+# (bits, asym) -> codes, scales, zeros that the exact computation gives
+_GPTQ_TINY_EXPECT = {
+    (4, True): ([[0, 15, 0, 15], [0, 15, 0, 13]],
+                [[0.10833740234375, 0.07135009765625], [0.0291595458984375, 0.019989013671875]],
+                [[8, 14], [15, 15]]),
+    (3, False): ([[1, 7, 1, 4], [1, 2, 3, 1]],
+                 [[0.291748046875, 0.330810546875], [0.291748046875, 0.09912109375]],
+                 None),
+}
+
+
+@pytest.mark.parametrize("bits,asym", [(4, True), (3, False)])
+def test_gptq_tiny_layer_against_exact_rationals(bits, asym):
+    X = np.array(_GPTQ_TINY_X, np.float16)
+    W = np.array(_GPTQ_TINY_W, np.float16)
+    Xq = [[Fraction(float(v)) for v in r] for r in X]
+    Wq = [[Fraction(float(v)) for v in r] for r in W]
+    codes, S, Z = _gptq_exact(Xq, Wq, bits, 2, asym)
+    e_codes, e_S, e_Z = _GPTQ_TINY_EXPECT[(bits, asym)]
+    assert codes == e_codes
+    assert [[float(s) for s in r] for r in S] == e_S
+    if asym:
+        assert [[int(z) for z in r] for r in Z] == e_Z
+    # the case separates the readings: parameters from the original weights
+    # give other scales and other codes
+    codes_o, S_o, _ = _gptq_exact(Xq, Wq, bits, 2, asym, params_from_original=True)
+    assert S_o != S and codes_o != codes
+    q = O.gptq(X.astype(np.float64), W, bits, 2, asym)
+    assert q.codes.tolist() == e_codes
+    assert q.scales.astype(np.float64).tolist() == e_S
+    if asym:
+        assert q.zeros.astype(np.float64).tolist() == [[float(z) for z in r] for r in e_Z]
+    else:
+        assert q.zeros is None
+
+
+# ---------------------------------------------------------------------------
+# The parity checker, the layer objective, activation decoding and the AWQ
+# scale floor, each against closed forms or exact arithmetic.
+# ---------------------------------------------------------------------------
+
+def test_rel_l2_closed_forms():
+    ref = np.array([3.0, 4.0])                         # ||ref|| = 5
+    assert O.rel_l2(ref, ref) == 0.0
+    assert O.rel_l2(np.array([4.0, 4.0]), ref) == 0.2   # ||(1, 0)|| / 5
+    assert abs(O.rel_l2(ref * 1.1, ref) - 0.1) < 1e-15
+    assert abs(O.rel_l2(np.array([[3.0, 4.0], [5.0, 12.0]]), np.array([[0.0, 0.0], [5.0, 12.0]])) - 5.0 / 13.0) < 1e-15
+    assert O.rel_l2(np.array([0.0, 2.0]), np.zeros(2)) == 2.0   # zero reference: the plain norm
+
+
+def test_reconstruction_loss_against_fractions():
+    rng = np.random.default_rng(12)
+    T, N, K = 3, 2, 64
+    X = rng.standard_normal((T, K)).astype(np.float16).astype(np.float64)
+    W = _random_groups(rng, N, K)
+    q = O.quantize(W, 3, 32, True)
+    total = Fraction(0)
+    for t in range(T):
+        for n in range(N):
+            d = Fraction(0)
+            for k in range(K):
+                g = k // 32
+                w_hat = (Fraction(int(q.codes[n, k])) - Fraction(float(q.zeros[n, g]))) * Fraction(float(q.scales[n, g]))
+                d += Fraction(float(X[t, k])) * (Fraction(float(W[n, k])) - w_hat)
+            total += d * d
+    got = O.reconstruction_loss(X, W, q)
+    assert abs(got - float(total)) <= 1e-12 * float(total)
+
+
+def test_activations_f64_decodes_bf16_bits_and_fp16_values():
+    bits = np.array([[0x3F80, 0xC000, 0x4049, 0x0000], [0x8000, 0x7F7F, 0x0001, 0xBF00]], np.uint16)
+    vals = O.activations_f64(bits, "bf16")
+    assert vals.dtype == np.float64 and vals.shape == (2, 4)
+    assert vals.tolist() == [[1.0, -2.0, 3.140625, 0.0], [0.0, 255 * 2.0 ** 120, 2.0 ** -133, -0.5]]
+    h = np.array([[1.0, -2.5, 65504.0, 2.0 ** -24]], np.float16)
+    assert O.activations_f64(h, "f16").tolist() == [[1.0, -2.5, 65504.0, 2.0 ** -24]]
+
+
+def test_awq_scale_floor_for_quiet_channels():
+    # channels whose mean |x| is below the floor 1e-4 are scaled as if it were
+    # 1e-4 (alpha = 1 returns the floored means themselves, rounded to fp32)
+    m = np.array([0.0, 5e-5, 1e-4, 2e-4, 1.0])
+    assert np.array_equal(O.awq_scale_for(m, 1.0), np.array([1e-4, 1e-4, 1e-4, 2e-4, 1.0], np.float32))
+    s = O.awq_scale_for(m, 0.5)
+    assert np.all(np.abs(s[:3].astype(np.float64) - 1e-2) <= 1e-2 * 2.0 ** -23)
+    # a channel that never fires still gets a finite, positive scale in the search
+    X = np.ones((4, 128))
+    X[:, 3] = 0.0
+    W = np.full((2, 128), 0.01, np.float16)
+    _, _, best_s = O.awq_search(X, W, 4, 128, True, 4)
+    assert np.all(np.isfinite(best_s)) and np.all(best_s > 0)

@@ -3,7 +3,10 @@
 Each case plants one mistake in a private copy of the oracle's source (a
 dropped term, a wrong sign, a wrong constant, swapped indices, a transposed
 operand), loads that copy as a separate module, and checks that at least one
-pin of ``test_oracle.py`` fails against it.  The real oracle is untouched.
+pin of ``test_oracle.py`` fails against it with an assertion.  A pin that
+crashes (a TypeError, a shape error) does not count as a catch, and a guard
+case runs every pin through the same harness against the unmutated oracle,
+where all of them must pass.  The real oracle is untouched.
 """
 import importlib.util
 import inspect
@@ -56,6 +59,14 @@ MUTATIONS = {
                                           "qg = quantize(W[:, k:k + group_size].astype(np.float32)"),
     "scale_not_fp16": ("S = np.divide(a, qmax, dtype=np.float32).astype(np.float16)",
                        "S = np.divide(a, qmax, dtype=np.float32).astype(np.float16) * np.float16(1.0009765625)"),
+    "rel_l2_squared": ("return float(num / den) if den > 0 else float(num)",
+                       "return float((num / den) ** 2) if den > 0 else float(num)"),
+    "reconstruction_loss_not_squared": ("return float(np.sum((X64 @ D.T) ** 2))",
+                                        "return float(np.sum(np.abs(X64 @ D.T)))"),
+    "bf16_bits_read_as_values": ("        return bf16_bits_to_f64(X)\n",
+                                 "        return np.asarray(X).astype(np.float64)\n"),
+    "awq_floor_1e-2": ("AWQ_SCALE_FLOOR = 1e-4", "AWQ_SCALE_FLOOR = 1e-2"),
+    "gptq_error_not_propagated": ("Wf[:, k + 1:] -= np.outer(err, U[k, k + 1:])", "pass"),
 }
 
 
@@ -74,7 +85,9 @@ def _mutant(name, old, new):
 
 
 def _pin_calls():
-    """Every pin in test_oracle.py with each of its parameter combinations."""
+    """Every pin in test_oracle.py with each of its parameter combinations.
+    A parametrize mark may name several arguments ("bits,asym,G"), whose
+    values are then tuples."""
     calls = []
     for fname, fn in inspect.getmembers(pins, inspect.isfunction):
         if not fname.startswith("test_"):
@@ -84,11 +97,35 @@ def _pin_calls():
         for m in marks:
             if m.name != "parametrize":
                 continue
-            argname, values = m.args[0], m.args[1]
-            combos = [dict(c, **{argname: v}) for c in combos for v in values]
+            argnames, values = m.args[0], m.args[1]
+            names = [a.strip() for a in argnames.split(",")] if isinstance(argnames, str) else list(argnames)
+            rows = [v if len(names) > 1 else (v,) for v in values]
+            assert all(len(r) == len(names) for r in rows), fname
+            combos = [dict(c, **dict(zip(names, r))) for c in combos for r in rows]
+        assert set(inspect.signature(fn).parameters) == set(combos[0]), fname
         for c in combos:
             calls.append((fname, fn, c))
     return calls
+
+
+def _run_pins():
+    """(caught, crashed): pins that failed with an assertion, and pins that
+    raised anything else."""
+    caught, crashed = [], []
+    for fname, fn, kwargs in _pin_calls():
+        try:
+            fn(**kwargs)
+        except AssertionError:
+            caught.append(fname)
+        except Exception as e:  # noqa: BLE001 - reported, never counted as a catch
+            crashed.append(f"{fname}: {type(e).__name__}: {e}")
+    return caught, crashed
+
+
+def test_every_pin_passes_on_the_unmutated_oracle_through_the_harness():
+    caught, crashed = _run_pins()
+    assert not caught and not crashed, (caught, crashed)
+    assert len(_pin_calls()) >= 70
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
@@ -96,10 +133,5 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
     old, new = MUTATIONS[name]
     mutant = _mutant(name, old, new)
     monkeypatch.setattr(pins, "O", mutant)
-    failed = []
-    for fname, fn, kwargs in _pin_calls():
-        try:
-            fn(**kwargs)
-        except Exception:  # an assertion or a crash: the pin rejects the mutant
-            failed.append(fname)
-    assert failed, f"no pin caught mutation {name}"
+    caught, crashed = _run_pins()
+    assert caught, f"no pin caught mutation {name} with an assertion (crashes: {crashed})"

@@ -264,13 +264,14 @@ woq_status woq_gptq_quantize_pack(const void* X, const void* W, int64_t T, int64
   if (!scales || !aligned(scales, 2)) return fail(WOQ_ERR_INVALID_ARGUMENT, "scales must be non-NULL, 2-byte aligned");
   if (asymmetric && (!zeros || !aligned(zeros, 2)))
     return fail(WOQ_ERR_INVALID_ARGUMENT, "zeros must be non-NULL and 2-byte aligned when asymmetric");
+  if (!asymmetric && zeros) return fail(WOQ_ERR_INVALID_ARGUMENT, "zeros must be NULL when symmetric");
   const size_t need = woq::gptq_workspace_bytes(T, N, K);
   if (!workspace || !aligned(workspace, 256))
     return fail(WOQ_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
   if (workspace_bytes < need)
     return fail(WOQ_ERR_INVALID_ARGUMENT, "workspace too small (%zu bytes, need %zu)", workspace_bytes, need);
   return from_hip(woq::launch_gptq(X, W, T, N, K, bits, group_size, asymmetric != 0, damp, packed, scales,
-                                   asymmetric ? zeros : nullptr, workspace, static_cast<hipStream_t>(stream)),
+                                   zeros, workspace, static_cast<hipStream_t>(stream)),
                   "gptq launch");
   WOQ_GUARD_END
 }

@@ -42,6 +42,40 @@ def packed_bytes(N: int, K: int, bits: int) -> int:
     return int(_lib.call("woq_packed_bytes", N, K, bits))
 
 
+def _check_quantizer(N: int, K: int, bits: int, group_size: int) -> None:
+    if bits not in (3, 4):
+        raise ValueError(f"bits must be 3 or 4 (got {bits})")
+    if N < 1 or K < 32 or K % 32 or group_size < 32 or group_size % 32 or K % group_size:
+        raise ValueError(f"need N >= 1, K a positive multiple of 32 and of group_size, group_size a multiple "
+                         f"of 32 (got N={N}, K={K}, group_size={group_size})")
+
+
+def _check_packed(packed: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor], N: int, K: int,
+                  bits: int, group_size: int) -> None:
+    """The packed set of an [N, K] matrix: uint8 codes of N * K * bits / 8
+    bytes, fp16 scales (and zeros) of N * (K / group_size) elements."""
+    _check_quantizer(N, K, bits, group_size)
+    if packed.dtype != torch.uint8 or packed.numel() != N * K * bits // 8:
+        raise ValueError(f"packed must be uint8 with N*K*bits/8 = {N * K * bits // 8} elements "
+                         f"(got {packed.dtype}, {packed.numel()})")
+    ng = N * (K // group_size)
+    for name, t in (("scales", scales), ("zeros", zeros)):
+        if t is not None and (t.dtype != torch.float16 or t.numel() != ng):
+            raise ValueError(f"{name} must be float16 with N*(K/group_size) = {ng} elements "
+                             f"(got {t.dtype}, {t.numel()})")
+
+
+def _check_act_scale(act_scale: Optional[torch.Tensor], K: int) -> None:
+    if act_scale is not None and (act_scale.dtype != torch.float32 or tuple(act_scale.shape) != (K,)):
+        raise ValueError(f"act_scale must be float32 of shape ({K},) (got {act_scale.dtype}, "
+                         f"{tuple(act_scale.shape)})")
+
+
+def _check_out(out: torch.Tensor, shape: Tuple[int, ...], dtype: torch.dtype, name: str) -> None:
+    if out.dtype != dtype or tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)} (got {out.dtype}, {tuple(out.shape)})")
+
+
 def quantize_pack(
     W: torch.Tensor,
     bits: int = 4,
@@ -54,14 +88,17 @@ def quantize_pack(
     if W.dtype != torch.float16 or W.dim() != 2:
         raise ValueError("W must be a 2-D float16 tensor")
     N, K = W.shape
-    if act_scale is not None and (act_scale.dtype != torch.float32 or act_scale.shape != (K,)):
-        raise ValueError("act_scale must be float32 [K]")
+    _check_quantizer(N, K, bits, group_size)
+    _check_act_scale(act_scale, K)
     if out is None:
         packed = torch.empty((N, K * bits // 8), dtype=torch.uint8, device=W.device)
         scales = torch.empty((N, K // group_size), dtype=torch.float16, device=W.device)
         zeros = torch.empty_like(scales) if asymmetric else None
     else:
         packed, scales, zeros = out
+        if (zeros is not None) != bool(asymmetric):
+            raise ValueError("out must hold zeros exactly when asymmetric")
+        _check_packed(packed, scales, zeros, N, K, bits, group_size)
     _require_gpu(W, act_scale, packed, scales, zeros)
     st = _lib.call("woq_quantize_pack", W.data_ptr(), _ptr(act_scale), N, K, bits, group_size, int(asymmetric),
                    packed.data_ptr(), scales.data_ptr(), _ptr(zeros), _stream(W))
@@ -84,6 +121,10 @@ def gemv(
     """y [N] = (x / s) @ w_hat^T for x [K] (fp16 or bf16)."""
     if x.dtype not in _DTYPE or x.numel() != K:
         raise ValueError("x must be fp16/bf16 with K elements")
+    _check_packed(packed, scales, zeros, N, K, bits, group_size)
+    _check_act_scale(act_scale, K)
+    if out is not None:
+        _check_out(out, (N,), x.dtype, "out")
     y = out if out is not None else torch.empty((N,), dtype=x.dtype, device=x.device)
     _require_gpu(x, act_scale, packed, scales, zeros, y)
     st = _lib.call("woq_w4a16_gemv", x.data_ptr(), _DTYPE[x.dtype], _ptr(act_scale), packed.data_ptr(),
@@ -109,6 +150,10 @@ def gemm(
     if X.dtype not in _DTYPE or X.dim() != 2 or X.shape[1] != K:
         raise ValueError("X must be fp16/bf16 [M, K]")
     M = X.shape[0]
+    _check_packed(packed, scales, zeros, N, K, bits, group_size)
+    _check_act_scale(act_scale, K)
+    if out is not None:
+        _check_out(out, (M, N), X.dtype, "out")
     Y = out if out is not None else torch.empty((M, N), dtype=X.dtype, device=X.device)
     _require_gpu(X, act_scale, packed, scales, zeros, Y)
     st = _lib.call("woq_w4a16_gemm", X.data_ptr(), _DTYPE[X.dtype], _ptr(act_scale), packed.data_ptr(),
@@ -128,6 +173,7 @@ def dequantize(
     group_size: int = 128,
 ) -> torch.Tensor:
     """w_hat = (u - Z) * S as float32 [N, K]."""
+    _check_packed(packed, scales, zeros, N, K, bits, group_size)
     out = torch.empty((N, K), dtype=torch.float32, device=packed.device)
     _require_gpu(packed, scales, zeros, out)
     st = _lib.call("woq_dequantize", packed.data_ptr(), scales.data_ptr(), _ptr(zeros), N, K, bits, group_size,

@@ -36,7 +36,7 @@ pmc_copy_fetch, pmc_copy_write under DIR) into profiles/gemv_traffic.json.
 `--gemm-only M,N,K` runs five GEMMs of one shape and nothing else, for
 rocprofv3 counter runs of a single GEMM kernel.
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--variants] [--no-rows]
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-rows]
 """
 from __future__ import annotations
 
@@ -76,7 +76,6 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--variants", action="store_true", help="also time 4/3-bit x sym/asym GEMV variants")
     p.add_argument("--extra", default=None, help="write per-config results (JSON lines) to this file")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-rows", action="store_true", help="skip the per-row timings of the other workloads")
@@ -190,8 +189,8 @@ def write_traffic(prof_dir, copy_mib):
 def burst_us(torch, launches, reps=3):
     """Average duration (us) of each launch when the callables in `launches`
     run back to back behind a queue prefill, HIP events on the launch stream;
-    the best of `reps` bursts."""
-    best = None
+    the mean over `reps` bursts."""
+    total = 0.0
     for _ in range(reps):
         torch.cuda.synchronize()
         torch.cuda._sleep(PREFILL_CYCLES // 4)
@@ -202,9 +201,8 @@ def burst_us(torch, launches, reps=3):
             f()
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / len(launches)
-        best = us if best is None else min(best, us)
-    return best
+        total += e0.elapsed_time(e1) * 1e3 / len(launches)
+    return total / reps
 
 
 def time_rows(torch, ops, synth, checks):
@@ -226,29 +224,51 @@ def time_rows(torch, ops, synth, checks):
             return u.view(np.float32).astype(np.float64)
         return Y.cpu().numpy().astype(np.float64)
 
-    def record(row, key, lin, Y, s, sel):
+    def record(row, key, lin, Y, s, sel, bits=4, G=128, asym=True, X=None, xdtype=None):
         """Sampled output columns `sel` of a row's result, for the oracle."""
-        checks.append(("gemm", row, key, np.ascontiguousarray(lin.W[sel]), lin.X, lin.xdtype, s, host_y(Y)[:, sel]))
+        checks.append(("gemm", row, key, np.ascontiguousarray(lin.W[sel]), lin.X if X is None else X,
+                       lin.xdtype if xdtype is None else xdtype, s, host_y(Y)[:, sel], (bits, G, asym)))
 
-    # Decode GEMVs of the LLaMA-2-7B linears with their AWQ scales (4-bit asym g128).
+    rows["ceilings"] = time_ceilings(torch, dev)
+
+    # Decode GEMVs of the LLaMA-2-7B linears with their AWQ scales, 4-bit and
+    # 3-bit asymmetric g128.
     llama = {}
-    for i in range(7):
-        lin = synth.llama7b_linear(i)
-        W = torch.from_numpy(lin.W).to(dev)
-        s = torch.from_numpy(lin.act_scale).to(dev)
-        x = torch.from_numpy(lin.X[0]).to(dev)
-        nb = gemv_bytes(lin.N, lin.K, 4, 128, True, act_scale=True)
-        R = rotate_count(nb)
-        sets = [ops.quantize_pack(W, 4, 128, True, s) for _ in range(R)]
-        y = torch.empty(lin.N, dtype=torch.float16, device=dev)
-        us = burst_us(torch, [lambda j=j: ops.gemv(x, *sets[j % R], lin.N, lin.K, 4, 128, s, out=y)
-                              for j in range(10 * R)])
-        sel = np.arange(0, lin.N, max(1, lin.N // 256))
-        llama[lin.name] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
-                        "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": nb}
-        record("llama7b_decode_gemv_awq", lin.name, lin, y[None, :], lin.act_scale, sel)
-        del sets, W
-    rows["llama7b_decode_gemv_awq"] = llama
+    for bits, row in ((4, "llama7b_decode_gemv_awq"), (3, "llama7b_decode_gemv_awq_3bit")):
+        per = {}
+        for i in range(7):
+            lin = synth.llama7b_linear(i)
+            W = torch.from_numpy(lin.W).to(dev)
+            s = torch.from_numpy(lin.act_scale).to(dev)
+            x = torch.from_numpy(lin.X[0]).to(dev)
+            nb = gemv_bytes(lin.N, lin.K, bits, 128, True, act_scale=True)
+            R = rotate_count(nb)
+            sets = [ops.quantize_pack(W, bits, 128, True, s) for _ in range(R)]
+            y = torch.empty(lin.N, dtype=torch.float16, device=dev)
+            us = burst_us(torch, [lambda j=j: ops.gemv(x, *sets[j % R], lin.N, lin.K, bits, 128, s, out=y)
+                                  for j in range(10 * R)])
+            sel = np.arange(0, lin.N, max(1, lin.N // 256))
+            per[lin.name] = {"us": round(us, 3), "gbs": round(nb / us / 1e3, 1),
+                             "frac_hbm": round(nb / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": nb}
+            record(row, lin.name, lin, y[None, :], lin.act_scale, sel, bits=bits)
+            del sets, W
+        rows[row] = per
+        if bits == 4:
+            llama = per
+
+    # The decode shape (M = 1, K = N = 8192) with the other quantizers of the
+    # workload: 4-bit symmetric, 3-bit asymmetric and symmetric, g128 (the
+    # headline 4-bit asymmetric figure is the bench value).
+    lin = synth.decode_8k()
+    var = {}
+    for bits, asym in ((4, False), (3, True), (3, False)):
+        ms, vb, y = time_gemv_variant(torch, ops, synth, lin, bits, asym)
+        key = f"{bits}bit_{'asym' if asym else 'sym'}"
+        var[key] = {"us": round(ms * 1e3, 3), "gbs": round(vb / (ms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(vb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": vb}
+        record("decode_gemv_quantizers_k8192_n8192", key, lin, y[None, :], None, np.arange(0, lin.N, 32),
+               bits=bits, asym=asym)
+    rows["decode_gemv_quantizers_k8192_n8192"] = var
 
     # Fused projections: q/k/v (N = 3 x 4096) and gate/up (N = 2 x 11008) share
     # the input and its AWQ scale, so one launch over the stacked rows serves
@@ -347,9 +367,12 @@ def time_rows(torch, ops, synth, checks):
         fl = 2 * lin.M * lin.N * lin.K
         entry = {"us": round(us, 1), "tflops": round(fl / us / 1e6, 1),
                  "frac_mfma": round(fl / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4), "flop": fl}
+        sel = np.arange(0, lin.N, lin.N // 96)
         if xdtype == "f16":
-            sel = np.arange(0, lin.N, lin.N // 96)
             record("prefill_gemm_m2048_k4096_n11008", xdtype, lin, Y, None, sel)
+        else:
+            Xb = X.view(torch.int16).cpu().numpy().view(np.uint16)
+            record("prefill_gemm_m2048_k4096_n11008", xdtype, lin, Y, None, sel, X=Xb, xdtype="bf16")
         pre[xdtype] = entry
     del sets, W
     rows["prefill_gemm_m2048_k4096_n11008"] = pre
@@ -419,6 +442,63 @@ def time_rows(torch, ops, synth, checks):
     return rows
 
 
+STREAM_SHAPES = [(b, t, u) for t in (256, 512, 1024) for b in (256, 512, 1024, 2048) for u in (1, 2, 4)]
+
+
+def time_ceilings(torch, dev):
+    """What the chip sustains with no decode at all, measured the same way as
+    the quantized kernels (HIP events around back-to-back launches):
+
+    * a read-only stream of the decode GEMV's bytes (35,684,352: codes, scales,
+      zeros, x, y at M = 1, K = N = 8192, 4-bit asym g128) over rotated
+      buffers, for each launch shape in STREAM_SHAPES (blocks, threads, loads
+      in flight per thread);
+    * an empty launch back to back (one 64-thread block, and 1024 blocks of
+      512 threads, the GEMV's launch shape);
+    * fp16 MFMA (v_mfma_f32_32x32x16_f16) on random operands, 512 workgroups
+      of 4 waves (two per compute unit), about 5 ms per launch."""
+    from weight_only_quantization_quantize_amd import _lib
+
+    lib = _lib.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    nb = gemv_bytes(8192, 8192, 4, 128, True)
+    R = rotate_count(nb)
+    bufs = [torch.randint(0, 255, (nb,), dtype=torch.uint8, device=dev) for _ in range(R)]
+    sink = torch.empty(2048 * 1024, dtype=torch.int32, device=dev)
+
+    def read(j, b, t, u):
+        _lib.check(lib.woq_probe_stream_read(bufs[j % R].data_ptr(), nb, b, t, u, sink.data_ptr(), 0, stream),
+                   "woq_probe_stream_read")
+
+    shapes = {}
+    for b, t, u in STREAM_SHAPES:
+        us = burst_us(torch, [lambda j=j, b=b, t=t, u=u: read(j, b, t, u) for j in range(4 * R)])
+        shapes[f"{b}x{t}x{u}"] = round(us, 3)
+    best = min(shapes, key=shapes.get)
+    out["stream_read_35684352B"] = {
+        "bytes": nb, "rotated_buffers": R, "us_by_shape_blocks_x_threads_x_unroll": shapes, "best_shape": best,
+        "best_us": shapes[best], "best_gbs": round(nb / shapes[best] / 1e3, 1),
+        "best_frac_hbm": round(nb / shapes[best] / 1e3 / HBM_PEAK_GBS, 4),
+        "gemv_shape_us": shapes["1024x512x4"]}
+    for b, t in ((1, 64), (1024, 512)):
+        us = burst_us(torch, [lambda b=b, t=t: _lib.check(lib.woq_probe_empty(b, t, stream), "woq_probe_empty")
+                              for _ in range(256)])
+        out[f"empty_launch_{b}x{t}"] = {"us": round(us, 3)}
+    src = torch.randn(1 << 19, device=dev).to(torch.float16)   # 1 MiB of N(0, 1) fp16 operands
+    msink = torch.empty(512 * 256, dtype=torch.float32, device=dev)
+    iters = 40000
+    launch = lambda: _lib.check(lib.woq_probe_mfma_rate(src.data_ptr(), 512, iters, msink.data_ptr(), 0, stream),
+                                "woq_probe_mfma_rate")
+    launch()
+    us = burst_us(torch, [launch, launch, launch], reps=2)
+    fl = 512 * 4 * iters * 4 * 2 * 32 * 32 * 16
+    out["mfma_f16_32x32x16_random_operands"] = {
+        "us": round(us, 1), "tflops": round(fl / us / 1e6, 1), "frac_mfma": round(fl / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)}
+    del bufs
+    return out
+
+
 def row_checks(checks, rows):
     """The oracle on the samples time_rows kept: relative L2 of each sampled
     GEMV/GEMM output against the fp64 oracle on the same dequantized weights,
@@ -427,8 +507,8 @@ def row_checks(checks, rows):
 
     for c in checks:
         if c[0] == "gemm":
-            _, row, key, Wsel, X, xdtype, s, ysel = c
-            _, _, _, q = O.quantize_pack(Wsel, 4, 128, True, s)
+            _, row, key, Wsel, X, xdtype, s, ysel, (bits, G, asym) = c
+            _, _, _, q = O.quantize_pack(Wsel, bits, G, asym, s)
             ref = O.gemm(O.activations_f64(X, xdtype), O.dequantize(q), s)
             rows[row][key]["rel_l2_sampled"] = float(f"{O.rel_l2(ysel, ref):.3g}")
         else:
@@ -463,17 +543,29 @@ def time_gemv_variant(torch, ops, synth, lin, bits, asym, iters=100):
     torch.cuda.synchronize()
     ms = t.mean_ms() / iters
     del sets
-    return ms, nb
+    return ms, nb, y
+
+
+def host_cores():
+    """Host threads available to this process: the affinity set, capped by the
+    job's OMP_NUM_THREADS share when that is set."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    return min(n, int(cap)) if cap and cap.isdigit() and int(cap) > 0 else n
 
 
 def cpu_baseline(lin, packed_gpu, bits, G, asym, y_gpu):
-    """Time the oracle (as it stands) on the host: unpack + dequantize + fp64
-    GEMV of the whole decode workload, single-threaded BLAS."""
-    from threadpoolctl import threadpool_limits
+    """Time the oracle (as it stands) on the host: one full quantize_pack and
+    one unpack + dequantize + fp64 GEMV of the whole decode workload, BLAS on
+    every host core this process may use (numpy's element-wise steps run on
+    one)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import woq_oracle as O
 
-    with threadpool_limits(limits=1):
+    cores = host_cores()
+    with threadpool_limits(limits=cores):
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         t0 = time.perf_counter()
         ref_packed, ref_scales, ref_zeros, q = O.quantize_pack(lin.W, bits, G, asym)
         t_quant = time.perf_counter() - t0
@@ -493,10 +585,11 @@ def cpu_baseline(lin, packed_gpu, bits, G, asym, y_gpu):
     base = {
         "value": nb / t_gemv / 1e9,
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
         "sample": (f"one full M=1 K=N={lin.K} GEMV from the packed weights (unpack + dequantize + fp64 matvec, "
-                   f"{t_gemv:.2f} s) and one full quantize_pack ({t_quant:.2f} s); numpy, BLAS limited to 1 thread"),
+                   f"{t_gemv:.2f} s) and one full quantize_pack ({t_quant:.2f} s); numpy, BLAS on {blas_threads} "
+                   f"threads ({cores} host cores), element-wise steps on 1"),
         "gemv_s": t_gemv,
         "quantize_pack_s": t_quant,
     }
@@ -635,15 +728,6 @@ def main():
             "bytes_per_launch": nb,
         },
     }
-
-    if args.variants:
-        var = {}
-        for b_, a_ in [(4, True), (4, False), (3, True), (3, False)]:
-            ms, vb = time_gemv_variant(torch, ops, synth, lin, b_, a_)
-            var[f"{b_}bit_{'asym' if a_ else 'sym'}"] = {
-                "gemv_us": round(ms * 1e3, 3), "gbs": round(vb / (ms * 1e-3) / 1e9, 1),
-                "pct_hbm_peak": round(100 * vb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2), "bytes": vb}
-        result["variants"] = var
 
     checks = []
     if not args.no_rows:

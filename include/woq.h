@@ -221,6 +221,32 @@ woq_status woq_gptq_quantize_pack(const void* X, const void* W, int64_t T, int64
                                   void* packed, void* scales, void* zeros,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Measurement aids.  Not part of the method: they measure the ceilings the
+ * quantized kernels are compared with.  A decode GEMV reads its weights once
+ * and does about one flop per byte, so its floor is the time to stream those
+ * bytes ("MIT 6.5940 Lab 4 + Lab 5", Lab 4 "Starting point and setup"); a
+ * large-batch GEMM is bound by the matrix units ("CMU 11-868 L19-L20",
+ * section "Back to the question: where does the speed come from?").
+ *
+ * woq_probe_stream_read: reads `bytes` bytes (a multiple of 16) at p (device,
+ *   16-byte aligned) once, as 16-byte nontemporal loads: blocks x threads
+ *   threads (threads a multiple of 64, at most 1024), each with `unroll`
+ *   (1, 2, 4 or 8) loads in flight per round.  The XOR of the words each
+ *   thread read is written to sink[thread] (device, blocks * threads uint32)
+ *   only when store != 0; with store == 0 sink is never written.
+ * woq_probe_empty: launches an empty kernel of blocks x threads threads.
+ * woq_probe_mfma_rate: blocks workgroups of 4 waves, each running `iters`
+ *   steps of 4 independent v_mfma_f32_32x32x16_f16 chains (2 * 32 * 32 * 16
+ *   flop each) on operands read from src (device, at least 1 MiB of fp16
+ *   data, 16-byte aligned); the sums go to sink (device, blocks * 256 floats)
+ *   only when store != 0.
+ * Asynchronous on stream; invalid arguments return WOQ_ERR_INVALID_ARGUMENT. */
+woq_status woq_probe_stream_read(const void* p, size_t bytes, int32_t blocks, int32_t threads, int32_t unroll,
+                                 void* sink, int32_t store, void* stream);
+woq_status woq_probe_empty(int32_t blocks, int32_t threads, void* stream);
+woq_status woq_probe_mfma_rate(const void* src, int32_t blocks, int32_t iters, float* sink, int32_t store,
+                               void* stream);
+
 /* Static text for a status code. */
 const char* woq_status_string(woq_status status);
 

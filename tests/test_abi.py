@@ -283,3 +283,26 @@ def test_hip_error_surfaces_without_a_device(lib):
     st = _qp(lib)
     assert st == _lib.WOQ_ERR_HIP
     assert "quantize_pack launch" in lib.woq_last_error().decode()
+
+
+@pytest.mark.parametrize(
+    "call, needle",
+    [
+        (lambda l: l.woq_probe_stream_read(None, 1024, 4, 256, 1, FAKE, 0, None), "p must be"),
+        (lambda l: l.woq_probe_stream_read(FAKE + 8, 1024, 4, 256, 1, FAKE, 0, None), "p must be"),
+        (lambda l: l.woq_probe_stream_read(FAKE, 1000, 4, 256, 1, FAKE, 0, None), "bytes must be"),
+        (lambda l: l.woq_probe_stream_read(FAKE, 1024, 0, 256, 1, FAKE, 0, None), "blocks must be"),
+        (lambda l: l.woq_probe_stream_read(FAKE, 1024, 4, 100, 1, FAKE, 0, None), "threads must be"),
+        (lambda l: l.woq_probe_stream_read(FAKE, 1024, 4, 256, 3, FAKE, 0, None), "unroll must be"),
+        (lambda l: l.woq_probe_stream_read(FAKE, 1024, 4, 256, 1, None, 0, None), "sink must be"),
+        (lambda l: l.woq_probe_empty(0, 64, None), "blocks must be"),
+        (lambda l: l.woq_probe_empty(1, 2048, None), "threads must be"),
+        (lambda l: l.woq_probe_mfma_rate(None, 4, 10, FAKE, 0, None), "src must be"),
+        (lambda l: l.woq_probe_mfma_rate(FAKE, 0, 10, FAKE, 0, None), "blocks must be"),
+        (lambda l: l.woq_probe_mfma_rate(FAKE, 4, 0, FAKE, 0, None), "iters must be"),
+        (lambda l: l.woq_probe_mfma_rate(FAKE, 4, 10, None, 0, None), "sink must be"),
+    ],
+)
+def test_probes_reject(lib, call, needle):
+    assert call(lib) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    assert needle in lib.woq_last_error().decode()

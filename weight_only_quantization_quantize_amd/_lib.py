@@ -40,6 +40,9 @@ SIGNATURES = {
     "woq_gptq_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "woq_gptq_quantize_pack": (_i32, [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_double, _vp, _vp, _vp,
                                       _vp, _sz, _vp]),
+    "woq_probe_stream_read": (_i32, [_vp, _sz, _i32, _i32, _i32, _vp, _i32, _vp]),
+    "woq_probe_empty": (_i32, [_i32, _i32, _vp]),
+    "woq_probe_mfma_rate": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp]),
     "woq_status_string": (ctypes.c_char_p, [_i32]),
     "woq_last_error": (ctypes.c_char_p, []),
 }

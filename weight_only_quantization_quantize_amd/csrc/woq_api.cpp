@@ -276,6 +276,44 @@ woq_status woq_gptq_quantize_pack(const void* X, const void* W, int64_t T, int64
   WOQ_GUARD_END
 }
 
+woq_status woq_probe_stream_read(const void* p, size_t bytes, int32_t blocks, int32_t threads, int32_t unroll,
+                                 void* sink, int32_t store, void* stream) {
+  WOQ_GUARD_BEGIN
+  if (!p || !aligned(p, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "p must be non-NULL and 16-byte aligned");
+  if (bytes < 16 || bytes % 16 != 0 || bytes > ((size_t)1 << 40))
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16 (got %zu)", bytes);
+  if (blocks < 1 || blocks > (1 << 20)) return fail(WOQ_ERR_INVALID_ARGUMENT, "blocks must be in [1, 2^20] (got %d)", blocks);
+  if (threads < 64 || threads > 1024 || threads % 64 != 0)
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "threads must be a multiple of 64 in [64, 1024] (got %d)", threads);
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8)
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "unroll must be 1, 2, 4 or 8 (got %d)", unroll);
+  if (!sink || !aligned(sink, 4)) return fail(WOQ_ERR_INVALID_ARGUMENT, "sink must be non-NULL and 4-byte aligned");
+  return from_hip(woq::launch_stream_read(p, (int64_t)bytes, blocks, threads, unroll, sink, store != 0,
+                                          static_cast<hipStream_t>(stream)),
+                  "stream_read launch");
+  WOQ_GUARD_END
+}
+
+woq_status woq_probe_empty(int32_t blocks, int32_t threads, void* stream) {
+  WOQ_GUARD_BEGIN
+  if (blocks < 1 || blocks > (1 << 20)) return fail(WOQ_ERR_INVALID_ARGUMENT, "blocks must be in [1, 2^20] (got %d)", blocks);
+  if (threads < 1 || threads > 1024) return fail(WOQ_ERR_INVALID_ARGUMENT, "threads must be in [1, 1024] (got %d)", threads);
+  return from_hip(woq::launch_empty(blocks, threads, static_cast<hipStream_t>(stream)), "empty launch");
+  WOQ_GUARD_END
+}
+
+woq_status woq_probe_mfma_rate(const void* src, int32_t blocks, int32_t iters, float* sink, int32_t store,
+                               void* stream) {
+  WOQ_GUARD_BEGIN
+  if (!src || !aligned(src, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "src must be non-NULL and 16-byte aligned");
+  if (blocks < 1 || blocks > (1 << 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "blocks must be in [1, 65536] (got %d)", blocks);
+  if (iters < 1 || iters > (1 << 24)) return fail(WOQ_ERR_INVALID_ARGUMENT, "iters must be in [1, 2^24] (got %d)", iters);
+  if (!sink || !aligned(sink, 4)) return fail(WOQ_ERR_INVALID_ARGUMENT, "sink must be non-NULL and 4-byte aligned");
+  return from_hip(woq::launch_mfma_rate(src, blocks, iters, sink, store != 0, static_cast<hipStream_t>(stream)),
+                  "mfma_rate launch");
+  WOQ_GUARD_END
+}
+
 const char* woq_status_string(woq_status status) {
   switch (status) {
     case WOQ_OK:

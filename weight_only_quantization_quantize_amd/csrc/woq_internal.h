@@ -85,6 +85,13 @@ hipError_t launch_gptq(const void* X, const void* W, int64_t T, int64_t N, int64
                        bool asymmetric, double damp, void* packed, void* scales, void* zeros, void* workspace,
                        hipStream_t stream);
 
+// Measurement aids (no quantization): a read-only stream over `bytes` bytes
+// with a given launch shape, an empty kernel, and back-to-back fp16 MFMAs.
+hipError_t launch_stream_read(const void* p, int64_t bytes, int blocks, int threads, int unroll, void* sink,
+                              int store, hipStream_t stream);
+hipError_t launch_empty(int blocks, int threads, hipStream_t stream);
+hipError_t launch_mfma_rate(const void* src, int blocks, int iters, float* sink, int store, hipStream_t stream);
+
 // Dequantize to fp32 (test aid).
 hipError_t launch_dequantize(const void* packed, const void* scales, const void* zeros, int64_t N,
                              int64_t K, int bits, int group_size, bool asymmetric, float* out,

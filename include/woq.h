@@ -187,6 +187,23 @@ woq_status woq_awq_search(const void* X, const void* W, int64_t T, int64_t N, in
                           double* losses, float* best_scale, int32_t* best_index,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* The AWQ exponent search above without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Arguments, outputs and results
+ * are those of woq_awq_search; the scratch is a static device array of
+ * woq_awq_search_noalloc_max_bytes() bytes (32 MiB) inside the library, one
+ * per GPU, held until the process ends.  Every call on a GPU uses that GPU's
+ * one array, so calls that overlap on one GPU (other streams or threads)
+ * race and must be serialized by the caller.  No allocation, free or
+ * allocating library routine is called.  Shapes whose search does not fit
+ * the array return WOQ_ERR_UNSUPPORTED (e.g. T x N fp32 reference output
+ * plus one packed set, scale and fp16 output must fit: 512 tokens of a
+ * 4096 x 4096 layer do). */
+size_t woq_awq_search_noalloc_max_bytes(void);
+woq_status woq_awq_search_noalloc(const void* X, const void* W, int64_t T, int64_t N, int64_t K,
+                                  int32_t bits, int32_t group_size, int32_t asymmetric, int32_t n_grid,
+                                  double* losses, float* best_scale, int32_t* best_index, void* stream);
+
 /* GPTQ into layout v1 ("CMU 11-868 L19-L20 Model Quantization", section
  * "The algorithm in four steps"; the layer-wise objective of "Quantising
  * Large Language Models ...", section "Post-training methods for 4-bit

@@ -306,3 +306,16 @@ def test_hip_error_surfaces_without_a_device(lib):
 def test_probes_reject(lib, call, needle):
     assert call(lib) == _lib.WOQ_ERR_INVALID_ARGUMENT
     assert needle in lib.woq_last_error().decode()
+
+
+def test_awq_search_noalloc_rejects_before_any_hip_call(lib):
+    assert lib.woq_awq_search_noalloc_max_bytes() == 32 << 20
+    call = lambda **kw: lib.woq_awq_search_noalloc(
+        kw.get("X", FAKE), FAKE, kw.get("T", 128), kw.get("N", 64), kw.get("K", 256), 4, 128, 1, kw.get("n", 4),
+        FAKE, FAKE, FAKE, None)
+    assert call(X=None) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    assert "X and W" in lib.woq_last_error().decode()
+    assert call(n=0) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    # a 4096 x 16384 fp32 reference output alone is 256 MiB: beyond the static scratch
+    assert call(T=4096, N=16384, K=8192) == _lib.WOQ_ERR_UNSUPPORTED
+    assert "static" in lib.woq_last_error().decode()

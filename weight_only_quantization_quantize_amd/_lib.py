@@ -37,6 +37,8 @@ SIGNATURES = {
     "woq_dequantize": (_i32, [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp]),
     "woq_awq_search_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
     "woq_awq_search": (_i32, [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "woq_awq_search_noalloc_max_bytes": (_sz, []),
+    "woq_awq_search_noalloc": (_i32, [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "woq_gptq_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "woq_gptq_quantize_pack": (_i32, [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, ctypes.c_double, _vp, _vp, _vp,
                                       _vp, _sz, _vp]),

@@ -17,11 +17,23 @@
 // compute units that one product's tiles would leave idle.  The reference
 // output X W^T (fp32, from a dense fp16 MFMA kernel) and the channel means
 // (fp64) are computed once.  Everything lives in the caller's workspace.
+#include <mutex>
+
 #include "woq_device.h"
 #include "woq_internal.h"
 
 namespace woq {
 namespace {
+
+// Scratch of the allocation-free search: a file-scope device array (each GPU
+// that loads the library holds its own copy until the process ends).  In
+// host code `scratch` only names the symbol; its device address on the
+// current device comes from hipGetSymbolAddress, taken once per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
@@ -172,9 +184,10 @@ struct AwqLayout {
   size_t packed_bytes, sz_elems, yq_elems;  // per batch entry
 };
 
-AwqLayout awq_layout(int64_t T, int64_t N, int64_t K, int bits, int G, bool asym) {
+AwqLayout awq_layout(int64_t T, int64_t N, int64_t K, int bits, int G, bool asym, int max_batch = 8) {
   AwqLayout L{};
-  L.batch = awq_batch(T, N, K, bits);
+  const int b = awq_batch(T, N, K, bits);
+  L.batch = b < max_batch ? b : max_batch;
   L.packed_bytes = (size_t)N * K * bits / 8;  // a multiple of 16 (K % 32 == 0)
   L.sz_elems = (size_t)N * (K / G);
   L.yq_elems = (size_t)T * N;
@@ -210,10 +223,36 @@ size_t awq_search_workspace_bytes(int64_t T, int64_t N, int64_t K, int bits, int
   return awq_layout(T, N, K, bits, group_size, asymmetric).total;
 }
 
+size_t awq_search_noalloc_max_bytes() { return kNoAllocScratchBytes; }
+
+// The most exponents per batched GEMM launch whose layout fits the static
+// scratch (the batch does not change any output: every batched tile runs the
+// same kernel code as a single product); 0 if not even one fits.
+int awq_noalloc_batch(int64_t T, int64_t N, int64_t K, int bits, int group_size, bool asymmetric) {
+  for (int b = 8; b >= 1; --b)
+    if (awq_layout(T, N, K, bits, group_size, asymmetric, b).total <= kNoAllocScratchBytes) return b;
+  return 0;
+}
+
+hipError_t awq_noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_awq_search(const void* X, const void* W, int64_t T, int64_t N, int64_t K, int bits,
                              int group_size, bool asymmetric, int n_grid, double* losses, float* best_scale,
-                             int32_t* best_index, void* workspace, hipStream_t stream) {
-  const AwqLayout L = awq_layout(T, N, K, bits, group_size, asymmetric);
+                             int32_t* best_index, void* workspace, hipStream_t stream, int max_batch) {
+  const AwqLayout L = awq_layout(T, N, K, bits, group_size, asymmetric, max_batch);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   double* m = reinterpret_cast<double*>(ws + L.m);
   float* s = reinterpret_cast<float*>(ws + L.s);

@@ -93,6 +93,25 @@ woq_status from_hip(hipError_t e, const char* what) {
     return fail(WOQ_ERR_INTERNAL, "internal error: unknown exception");      \
   }
 
+// Arguments of the AWQ search other than its scratch.
+woq_status check_awq_args(const void* X, const void* W, int64_t T, int64_t N, int64_t K, int32_t bits,
+                          int32_t group_size, int32_t n_grid, const double* losses, const float* best_scale,
+                          const int32_t* best_index) {
+  WOQ_TRY(check_qparams(N, K, bits, group_size));
+  if (T < 1) return fail(WOQ_ERR_INVALID_ARGUMENT, "T must be >= 1 (got %lld)", (long long)T);
+  if (T > INT32_MAX / 2 || T * N > (int64_t)1 << 40)
+    return fail(WOQ_ERR_UNSUPPORTED, "T x N too large for this library (T=%lld, N=%lld)", (long long)T, (long long)N);
+  if (n_grid < 1 || n_grid > 64) return fail(WOQ_ERR_INVALID_ARGUMENT, "n_grid must be in [1, 64] (got %d)", n_grid);
+  if (!X || !W) return fail(WOQ_ERR_INVALID_ARGUMENT, "X and W must not be NULL");
+  if (!aligned(X, 16) || !aligned(W, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "X and W must be 16-byte aligned");
+  if (!losses || !aligned(losses, 8)) return fail(WOQ_ERR_INVALID_ARGUMENT, "losses must be non-NULL, 8-byte aligned");
+  if (!best_scale || !aligned(best_scale, 16))
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "best_scale must be non-NULL, 16-byte aligned");
+  if (!best_index || !aligned(best_index, 4))
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "best_index must be non-NULL, 4-byte aligned");
+  return WOQ_OK;
+}
+
 // GPTQ runs 128-column blocks whose groups either split a block evenly or
 // cover whole blocks; the factorization uses 64-wide panels.
 woq_status check_gptq(int64_t T, int64_t N, int64_t K, int32_t bits, int32_t group_size) {
@@ -224,18 +243,7 @@ woq_status woq_awq_search(const void* X, const void* W, int64_t T, int64_t N, in
                           int32_t group_size, int32_t asymmetric, int32_t n_grid, double* losses, float* best_scale,
                           int32_t* best_index, void* workspace, size_t workspace_bytes, void* stream) {
   WOQ_GUARD_BEGIN
-  WOQ_TRY(check_qparams(N, K, bits, group_size));
-  if (T < 1) return fail(WOQ_ERR_INVALID_ARGUMENT, "T must be >= 1 (got %lld)", (long long)T);
-  if (T > INT32_MAX / 2 || T * N > (int64_t)1 << 40)
-    return fail(WOQ_ERR_UNSUPPORTED, "T x N too large for this library (T=%lld, N=%lld)", (long long)T, (long long)N);
-  if (n_grid < 1 || n_grid > 64) return fail(WOQ_ERR_INVALID_ARGUMENT, "n_grid must be in [1, 64] (got %d)", n_grid);
-  if (!X || !W) return fail(WOQ_ERR_INVALID_ARGUMENT, "X and W must not be NULL");
-  if (!aligned(X, 16) || !aligned(W, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "X and W must be 16-byte aligned");
-  if (!losses || !aligned(losses, 8)) return fail(WOQ_ERR_INVALID_ARGUMENT, "losses must be non-NULL, 8-byte aligned");
-  if (!best_scale || !aligned(best_scale, 16))
-    return fail(WOQ_ERR_INVALID_ARGUMENT, "best_scale must be non-NULL, 16-byte aligned");
-  if (!best_index || !aligned(best_index, 4))
-    return fail(WOQ_ERR_INVALID_ARGUMENT, "best_index must be non-NULL, 4-byte aligned");
+  WOQ_TRY(check_awq_args(X, W, T, N, K, bits, group_size, n_grid, losses, best_scale, best_index));
   const size_t need = woq::awq_search_workspace_bytes(T, N, K, bits, group_size, asymmetric != 0);
   if (!workspace || !aligned(workspace, 256))
     return fail(WOQ_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
@@ -246,6 +254,29 @@ woq_status woq_awq_search(const void* X, const void* W, int64_t T, int64_t N, in
                   "awq_search launch");
   WOQ_GUARD_END
 }
+
+woq_status woq_awq_search_noalloc(const void* X, const void* W, int64_t T, int64_t N, int64_t K, int32_t bits,
+                                  int32_t group_size, int32_t asymmetric, int32_t n_grid, double* losses,
+                                  float* best_scale, int32_t* best_index, void* stream) {
+  WOQ_GUARD_BEGIN
+  WOQ_TRY(check_awq_args(X, W, T, N, K, bits, group_size, n_grid, losses, best_scale, best_index));
+  const int batch = woq::awq_noalloc_batch(T, N, K, bits, group_size, asymmetric != 0);
+  if (batch < 1)
+    return fail(WOQ_ERR_UNSUPPORTED,
+                "awq_search_noalloc: this shape needs more scratch than the static %zu bytes "
+                "(woq_awq_search with a workspace of %zu bytes takes it)",
+                woq::awq_search_noalloc_max_bytes(),
+                woq::awq_search_workspace_bytes(T, N, K, bits, group_size, asymmetric != 0));
+  void* scratch = nullptr;
+  const hipError_t e = woq::awq_noalloc_scratch(&scratch);
+  if (e != hipSuccess) return from_hip(e, "awq_search_noalloc scratch address");
+  return from_hip(woq::launch_awq_search(X, W, T, N, K, bits, group_size, asymmetric != 0, n_grid, losses, best_scale,
+                                         best_index, scratch, static_cast<hipStream_t>(stream), batch),
+                  "awq_search_noalloc launch");
+  WOQ_GUARD_END
+}
+
+size_t woq_awq_search_noalloc_max_bytes(void) { return woq::awq_search_noalloc_max_bytes(); }
 
 size_t woq_gptq_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t bits, int32_t group_size) {
   if (check_gptq(T, N, K, bits, group_size) != WOQ_OK) return 0;

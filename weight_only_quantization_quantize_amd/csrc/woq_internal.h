@@ -69,9 +69,18 @@ hipError_t launch_gemm_skinny(const void* X, int xdtype, const float* act_scale,
 
 // AWQ exponent search (scratch in the caller's workspace).
 size_t awq_search_workspace_bytes(int64_t T, int64_t N, int64_t K, int bits, int group_size, bool asymmetric);
+// max_batch caps the exponents per batched GEMM launch (and with it the
+// workspace layout); it changes no output.
 hipError_t launch_awq_search(const void* X, const void* W, int64_t T, int64_t N, int64_t K, int bits,
                              int group_size, bool asymmetric, int n_grid, double* losses, float* best_scale,
-                             int32_t* best_index, void* workspace, hipStream_t stream);
+                             int32_t* best_index, void* workspace, hipStream_t stream, int max_batch = 8);
+// The allocation-free search: its scratch is a static device array of
+// awq_search_noalloc_max_bytes() bytes; awq_noalloc_batch gives the batch
+// that fits it (0: the shape does not fit); awq_noalloc_scratch the array's
+// address on the current device.
+size_t awq_search_noalloc_max_bytes();
+int awq_noalloc_batch(int64_t T, int64_t N, int64_t K, int bits, int group_size, bool asymmetric);
+hipError_t awq_noalloc_scratch(void** ptr);
 
 // Y[m, n] = sum_k A[m, k] B[n, k] in fp32 for fp16 A [M, K], B [N, K]
 // (K % 16 == 0): the dense MFMA product the AWQ search uses for its

@@ -1,4 +1,4 @@
-"""CPU oracle for group-wise weight-only RTN quantization, the layout-v1 packed
+"""CPU oracle for group-wise weight-only RTN quantization, the layout-v2 packed
 stream, dequantization, and the dequantize-GEMV/GEMM that consumes it.
 
 TEST INFRASTRUCTURE ONLY.  This module is the slow, plain, obviously-correct
@@ -70,8 +70,8 @@ __all__ = [
     "Quantized",
     "fold_act_scale",
     "quantize",
-    "pack_v1",
-    "unpack_v1",
+    "pack_v2",
+    "unpack_v2",
     "packed_row_bytes",
     "dequantize",
     "bf16_bits_to_f64",
@@ -195,17 +195,18 @@ def packed_row_bytes(K: int, bits: int) -> int:
     return K * bits // 8
 
 
-def pack_v1(codes: np.ndarray, bits: int) -> np.ndarray:
-    """Pack unsigned codes [N, K] into layout v1, uint8 [N, K*bits/8].
+def pack_v2(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack unsigned codes [N, K] into layout v2, uint8 [N, K*bits/8].
 
-    Layout v1 (little-endian 32-bit words, rows back to back):
+    Layout v2 (little-endian 32-bit words, rows back to back):
 
-    * 4-bit: word j of a row holds k in [8j, 8j+8); the code of
-      k = 8j + 2t + h (t in 0..3, h in 0..1) sits at bits [16h + 4t, 16h + 4t + 4).
+    * 4-bit (as in layout v1): word j of a row holds k in [8j, 8j+8); the code
+      of k = 8j + 2t + h (t in 0..3, h in 0..1) sits at bits
+      [16h + 4t, 16h + 4t + 4).
     * 3-bit: a 12-byte unit j (words w0, w1, w2) holds k in [32j, 32j+32); for
-      i = k - 32j = 2t + h (t in 0..15, h in 0..1) the two low bits of the
-      code sit in word w_(t // 8) at bits [16h + 2(t % 8), +2) and the high bit
-      in w2 at bit 16h + t.
+      i = k - 32j = 2t + h (t in 0..15, h in 0..1) the code of pair t < 15 sits
+      whole in word w_(t // 5) at bits [16h + 3(t % 5), +3); the code of pair
+      15 is split, its bit b (b = 0, 1, 2) at bit 16h + 15 of word w_b.
 
     Written element by element from that definition (slow on purpose).
     """
@@ -225,17 +226,20 @@ def pack_v1(codes: np.ndarray, bits: int) -> np.ndarray:
         for j in range(K // 32):
             for i in range(32):
                 t, h = divmod(i, 2)
-                u = codes[:, 32 * j + i].astype(np.uint32)
-                words[:, j, t // 8] |= (u & 3) << np.uint32(16 * h + 2 * (t % 8))
-                words[:, j, 2] |= ((u >> 2) & 1) << np.uint32(16 * h + t)
+                u = codes[:, 32 * j + i].astype(np.uint32) & 7
+                if t < 15:
+                    words[:, j, t // 5] |= u << np.uint32(16 * h + 3 * (t % 5))
+                else:
+                    for b in range(3):
+                        words[:, j, b] |= ((u >> np.uint32(b)) & 1) << np.uint32(16 * h + 15)
         words = words.reshape(N, -1)
     else:
-        raise ValueError("layout v1 is defined for 3 and 4 bits")
+        raise ValueError("layout v2 is defined for 3 and 4 bits")
     return np.ascontiguousarray(words.astype("<u4")).view(np.uint8).reshape(N, packed_row_bytes(K, bits))
 
 
-def unpack_v1(packed: np.ndarray, bits: int, K: int) -> np.ndarray:
-    """Inverse of :func:`pack_v1`: uint8 [N, K*bits/8] -> codes uint8 [N, K]."""
+def unpack_v2(packed: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """Inverse of :func:`pack_v2`: uint8 [N, K*bits/8] -> codes uint8 [N, K]."""
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     N = packed.shape[0]
     words = packed.reshape(N, -1).view("<u4").astype(np.uint32)
@@ -250,11 +254,13 @@ def unpack_v1(packed: np.ndarray, bits: int, K: int) -> np.ndarray:
         for j in range(K // 32):
             for i in range(32):
                 t, h = divmod(i, 2)
-                lo = (words[:, j, t // 8] >> np.uint32(16 * h + 2 * (t % 8))) & 3
-                hi = (words[:, j, 2] >> np.uint32(16 * h + t)) & 1
-                codes[:, 32 * j + i] = lo | (hi << 2)
+                if t < 15:
+                    u = (words[:, j, t // 5] >> np.uint32(16 * h + 3 * (t % 5))) & 7
+                else:
+                    u = sum(((words[:, j, b] >> np.uint32(16 * h + 15)) & 1) << np.uint32(b) for b in range(3))
+                codes[:, 32 * j + i] = u
     else:
-        raise ValueError("layout v1 is defined for 3 and 4 bits")
+        raise ValueError("layout v2 is defined for 3 and 4 bits")
     return codes
 
 
@@ -306,9 +312,9 @@ def gemm(X64: np.ndarray, w_hat: np.ndarray, act_scale: Optional[np.ndarray] = N
 
 
 def quantize_pack(W, bits, group_size, asymmetric, act_scale=None):
-    """quantize + pack_v1: returns (packed uint8 [N, K*bits/8], scales f16, zeros f16|None, Quantized)."""
+    """quantize + pack_v2: returns (packed uint8 [N, K*bits/8], scales f16, zeros f16|None, Quantized)."""
     q = quantize(W, bits, group_size, asymmetric, act_scale)
-    return pack_v1(q.codes, bits), q.scales, q.zeros, q
+    return pack_v2(q.codes, bits), q.scales, q.zeros, q
 
 
 def rel_l2(y: np.ndarray, y_ref: np.ndarray) -> float:

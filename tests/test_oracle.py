@@ -275,41 +275,58 @@ def test_underflowing_scale():
 
 
 # ---------------------------------------------------------------------------
-# Packed layout v1.
+# Packed layout v2 (3-bit pairs kept whole; 4-bit as in v1).
 # ---------------------------------------------------------------------------
 
-def test_layout_v1_fixed_words():
-    g = _load("layout_v1_words.json")
+def test_layout_v2_fixed_words():
+    g = _load("layout_v2_words.json")
     u4 = (np.arange(16) % 16).astype(np.uint8)[None, :]
-    w4 = O.pack_v1(u4, 4).view("<u4")[0].tolist()
+    w4 = O.pack_v2(u4, 4).view("<u4")[0].tolist()
     assert w4 == [int(h, 16) for h in g["four_bit"]["words_hex"]]
     u3 = (np.arange(32) % 8).astype(np.uint8)[None, :]
-    w3 = O.pack_v1(u3, 3).view("<u4")[0].tolist()
+    w3 = O.pack_v2(u3, 3).view("<u4")[0].tolist()
     assert w3 == [int(h, 16) for h in g["three_bit"]["words_hex"]]
 
 
 @pytest.mark.parametrize("bits", [3, 4])
-def test_layout_v1_round_trip_and_single_code(bits):
+def test_layout_v2_round_trip_and_single_code(bits):
     rng = np.random.default_rng(bits)
     u = rng.integers(0, 2 ** bits, size=(7, 256), dtype=np.uint8)
-    p = O.pack_v1(u, bits)
+    p = O.pack_v2(u, bits)
     assert p.shape == (7, 256 * bits // 8)
-    assert np.array_equal(O.unpack_v1(p, bits, 256), u)
+    assert np.array_equal(O.unpack_v2(p, bits, 256), u)
     # a lone code lands on exactly the bits the definition names
-    for k in (0, 1, 2, 7, 13, 31, 200, 255):
-        one = np.zeros((1, 256), np.uint8)
-        one[0, k] = 2 ** bits - 1
-        words = O.pack_v1(one, bits).view("<u4")[0]
-        if bits == 4:
-            j, r = divmod(k, 8)
-            t, h = divmod(r, 2)
-            expect = {j: 0xF << (16 * h + 4 * t)}
-        else:
-            j, i = divmod(k, 32)
-            t, h = divmod(i, 2)
-            expect = {3 * j + t // 8: 3 << (16 * h + 2 * (t % 8)), 3 * j + 2: 1 << (16 * h + t)}
-        nz = {int(i): int(v) for i, v in enumerate(words) if v}
-        assert nz == expect
+    for k in (0, 1, 2, 7, 13, 28, 29, 30, 31, 200, 255):
+        for code in range(1, 2 ** bits):
+            one = np.zeros((1, 256), np.uint8)
+            one[0, k] = code
+            words = O.pack_v2(one, bits).view("<u4")[0]
+            if bits == 4:
+                j, r = divmod(k, 8)
+                t, h = divmod(r, 2)
+                expect = {j: code << (16 * h + 4 * t)}
+            else:
+                j, i = divmod(k, 32)
+                t, h = divmod(i, 2)
+                if t < 15:
+                    expect = {3 * j + t // 5: code << (16 * h + 3 * (t % 5))}
+                else:
+                    expect = {3 * j + b: 1 << (16 * h + 15) for b in range(3) if (code >> b) & 1}
+            nz = {int(i): int(v) for i, v in enumerate(words) if v}
+            assert nz == expect, (k, code)
+
+
+def test_layout_v2_three_bit_pairs_decode_with_one_mask():
+    # the property the layout is for: pair t < 15 of a unit is one 3-bit field
+    # in each 16-bit half of its word, (w >> 3 (t % 5)) & 0x00070007
+    rng = np.random.default_rng(9)
+    u = rng.integers(0, 8, size=(3, 64), dtype=np.uint8)
+    words = O.pack_v2(u, 3).view("<u4").reshape(3, 2, 3)
+    for j in range(2):
+        for t in range(15):
+            f = (words[:, j, t // 5] >> (3 * (t % 5))) & 0x00070007
+            assert np.array_equal(f & 0xFFFF, u[:, 32 * j + 2 * t])
+            assert np.array_equal(f >> 16, u[:, 32 * j + 2 * t + 1])
 
 
 # ---------------------------------------------------------------------------

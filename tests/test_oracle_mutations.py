@@ -31,8 +31,10 @@ MUTATIONS = {
     "sym_bias_dropped": ("u = (q + half).astype(np.uint8)", "u = (q + half - 1).astype(np.uint8)"),
     "zero_range_rule_dropped": ("r = np.where(r == 0, np.float32(1), r)", "r = r"),
     "pack_nibble_order": ("<< np.uint32(16 * h + 4 * t)\n", "<< np.uint32(8 * h + 4 * t)\n"),
-    "pack3_high_bit": ("words[:, j, 2] |= ((u >> 2) & 1) << np.uint32(16 * h + t)",
-                       "words[:, j, 2] |= ((u >> 2) & 1) << np.uint32(16 * (1 - h) + t)"),
+    "pack3_pair_field": ("words[:, j, t // 5] |= u << np.uint32(16 * h + 3 * (t % 5))",
+                         "words[:, j, t // 5] |= u << np.uint32(16 * h + 3 * (t % 4))"),
+    "pack3_last_pair_bits": ("words[:, j, b] |= ((u >> np.uint32(b)) & 1) << np.uint32(16 * h + 15)",
+                             "words[:, j, 2 - b] |= ((u >> np.uint32(b)) & 1) << np.uint32(16 * h + 15)"),
     "dequant_zero_dropped": ("return (q.codes.astype(np.float64) - Z) * S",
                              "return q.codes.astype(np.float64) * S"),
     "gemm_transposed": ("return X64 @ np.asarray(w_hat, dtype=np.float64).T",

@@ -570,7 +570,7 @@ def cpu_baseline(lin, packed_gpu, bits, G, asym, y_gpu):
         ref_packed, ref_scales, ref_zeros, q = O.quantize_pack(lin.W, bits, G, asym)
         t_quant = time.perf_counter() - t0
         t0 = time.perf_counter()
-        codes = O.unpack_v1(ref_packed, bits, lin.K)
+        codes = O.unpack_v2(ref_packed, bits, lin.K)
         qq = O.Quantized(codes, ref_scales, ref_zeros, bits, G, asym)
         y_ref = O.gemm(lin.X.astype(np.float64), O.dequantize(qq))[0]
         t_gemv = time.perf_counter() - t0

@@ -34,17 +34,19 @@
  *               u = clip(rne(w / S) + Z, 0, 2^b-1);  S == 0 -> Z = u = 0.
  *   dequantized weight: w_hat = (u - Z) * S.
  *
- * Packed layout v1 (WOQ_LAYOUT_V1).  Rows n = 0..N-1 back to back, each
+ * Packed layout v2 (WOQ_LAYOUT_V2).  Rows n = 0..N-1 back to back, each
  * K*bits/8 bytes; groups are contiguous along K starting at k = 0.  Words are
  * little-endian 32-bit.
- *   4-bit: word j of a row holds k in [8j, 8j+8); the code of
- *          k = 8j + 2t + h (t = 0..3, h = 0..1) is at bits [16h+4t, 16h+4t+4).
- *          (w >> 4t) & 0x000F000F therefore yields the pair (k, k+1) in the
- *          two 16-bit halves of a register.
+ *   4-bit (unchanged from layout v1): word j of a row holds k in [8j, 8j+8);
+ *          the code of k = 8j + 2t + h (t = 0..3, h = 0..1) is at bits
+ *          [16h+4t, 16h+4t+4).  (w >> 4t) & 0x000F000F therefore yields the
+ *          pair (k, k+1) in the two 16-bit halves of a register.
  *   3-bit: a 12-byte unit j (words w0, w1, w2) holds k in [32j, 32j+32); for
- *          i = k - 32j = 2t + h (t = 0..15, h = 0..1) the low two bits of the
- *          code are in w_(t/8) at bits [16h + 2(t%8), +2) and the high bit in
- *          w2 at bit 16h + t.
+ *          i = k - 32j = 2t + h (t = 0..15, h = 0..1) the whole code of pair
+ *          t < 15 is in w_(t/5) at bits [16h + 3(t%5), +3), so
+ *          (w >> 3(t%5)) & 0x00070007 yields pair t; the code of pair 15 is
+ *          split, its bit b (b = 0..2) at bit 16h + 15 of w_b.  (Layout v1
+ *          kept two low bits and the high bit of a pair in different words.)
  *   scales: fp16 [N, K/G] row-major.  zeros: fp16 [N, K/G] row-major holding
  *          the integer Z (asymmetric only).
  *
@@ -76,7 +78,7 @@
 extern "C" {
 #endif
 
-#define WOQ_LAYOUT_V1 1
+#define WOQ_LAYOUT_V2 2
 
 typedef enum woq_status {
   WOQ_OK = 0,
@@ -89,7 +91,7 @@ typedef enum woq_status {
 /* Activation / output element type. */
 typedef enum woq_dtype { WOQ_F16 = 0, WOQ_BF16 = 1 } woq_dtype;
 
-/* Layout version produced and consumed by this library (WOQ_LAYOUT_V1). */
+/* Layout version produced and consumed by this library (WOQ_LAYOUT_V2). */
 int32_t woq_layout_version(void);
 
 /* Bytes of the packed code array for an [N, K] matrix: N * K * bits / 8.
@@ -110,7 +112,7 @@ size_t woq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits, int32_
  *   W         : fp16 [N, K]
  *   act_scale : fp32 [K] AWQ scale s multiplied into column k before the
  *               group statistics, or NULL
- *   packed    : out, uint8 [N, K*bits/8] in layout v1
+ *   packed    : out, uint8 [N, K*bits/8] in layout v2
  *   scales    : out, fp16 [N, K/group_size]
  *   zeros     : out, fp16 [N, K/group_size] when asymmetric, else NULL
  * Bit-exact with the definition above (IEEE division, RNE everywhere). */
@@ -204,7 +206,7 @@ woq_status woq_awq_search_noalloc(const void* X, const void* W, int64_t T, int64
                                   int32_t bits, int32_t group_size, int32_t asymmetric, int32_t n_grid,
                                   double* losses, float* best_scale, int32_t* best_index, void* stream);
 
-/* GPTQ into layout v1 ("CMU 11-868 L19-L20 Model Quantization", section
+/* GPTQ into layout v2 ("CMU 11-868 L19-L20 Model Quantization", section
  * "The algorithm in four steps"; the layer-wise objective of "Quantising
  * Large Language Models ...", section "Post-training methods for 4-bit
  * weights").

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_size_queries(lib):
-    assert lib.woq_layout_version() == 1
+    assert lib.woq_layout_version() == 2
     assert lib.woq_packed_bytes(8192, 8192, 4) == 8192 * 4096
     assert lib.woq_packed_bytes(8192, 8192, 3) == 8192 * 3072
     assert lib.woq_packed_bytes(4096, 11008, 3) == 4096 * 11008 * 3 // 8

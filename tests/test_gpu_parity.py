@@ -187,7 +187,7 @@ def test_quantize_pack_worked_example():
     W = np.zeros((1, 128), np.float16)
     W[0, :6] = np.array([-0.89, 0.16, 0.08, -0.13, 0.16, -0.54], np.float32).astype(np.float16)
     packed, scales, zeros = ops.quantize_pack(gpu_f16(W), 4, 128, False)
-    codes = O.unpack_v1(packed.cpu().numpy(), 4, 128)
+    codes = O.unpack_v2(packed.cpu().numpy(), 4, 128)
     assert (codes[0, :6].astype(int) - 8).tolist() == [-7, 1, 1, -1, 1, -4]
     assert abs(float(scales.cpu().numpy()[0, 0]) - 0.127) < 5e-4
 
@@ -710,14 +710,14 @@ def test_awq_search_matches_oracle(T, N, K, bits, asym):
 
 
 # ---------------------------------------------------------------------------
-# GPTQ into layout v1
+# GPTQ into layout v2
 # ---------------------------------------------------------------------------
 
 def _gptq_gpu(X, W, bits, G, asym):
     packed, scales, zeros = ops.gptq(gpu_f16(X), gpu_f16(W), bits, G, asym)
     torch.cuda.synchronize()
     K = W.shape[1]
-    codes = O.unpack_v1(packed.cpu().numpy(), bits, K)
+    codes = O.unpack_v2(packed.cpu().numpy(), bits, K)
     zs = None if zeros is None else zeros.cpu().numpy()
     return O.Quantized(codes, scales.cpu().numpy(), zs, bits, G, asym), (packed, scales, zeros)
 

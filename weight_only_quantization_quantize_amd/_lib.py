@@ -20,7 +20,7 @@ WOQ_ERR_HIP = 3
 WOQ_ERR_INTERNAL = 4
 WOQ_F16 = 0
 WOQ_BF16 = 1
-WOQ_LAYOUT_V1 = 1
+WOQ_LAYOUT_V2 = 2
 
 _i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 

@@ -1,7 +1,7 @@
 // Dequantization w_hat = (u - Z) * S to fp32, one thread per 32-weight chunk.
 // The second half of pseudo-quantization ("MIT 6.5940 Lab 4 + Lab 5", Lab 4
 // "Starting point and setup"); exact because |u - Z| < 16 and S carries 11
-// significant bits.  Used to check the decode of layout v1 in isolation.
+// significant bits.  Used to check the decode of layout v2 in isolation.
 #include "woq_device.h"
 #include "woq_internal.h"
 

@@ -96,15 +96,15 @@ __device__ inline void dequant_pair_split(uint32_t codes2, float Z, float S, flo
 
 // Code pair t (K offsets 2t, 2t + 1 of this thread's codes) in the low bits of
 // each 16-bit half.  4-bit: word t / 4 holds 8 codes, pair t % 4 at bits
-// [4 (t % 4)] and [16 + 4 (t % 4)].  3-bit: w[0..1] are the low-bit words of
-// the 32-code unit (pairs 0..7 and 8..15), w[2] its high-bit word.
+// [4 (t % 4)] and [16 + 4 (t % 4)].  3-bit: w[0..2] are the three words of the
+// 32-code unit and the thread's codes start at pair pair_base of the unit (0,
+// or 8 when two threads share a unit).
 template <int BITS>
-__device__ inline uint32_t code_pair(const uint32_t* w, int t, int hi_base) {
+__device__ inline uint32_t code_pair(const uint32_t* w, int t, int pair_base) {
   if constexpr (BITS == 4) {
     return (w[t >> 2] >> (4 * (t & 3))) & 0x000F000Fu;
   } else {
-    const uint32_t lo2 = (w[t >> 3] >> (2 * (t & 7))) & 0x00030003u;
-    return lo2 | (((w[2] >> (hi_base + t)) & 0x00010001u) << 2);
+    return pair3(w[0], w[1], w[2], pair_base + t, 0u);
   }
 }
 
@@ -202,13 +202,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
       }
     } else {
       const uint32_t* p = reinterpret_cast<const uint32_t*>(b_src + (kc / 32) * 12);
-      if constexpr (TL::kCodes == 32) {
-        R.w[0] = p[0];
-        R.w[1] = p[1];
-      } else {
-        R.w[0] = p[(kc / 16) & 1];  // low-bit word of this half of the unit
-        R.w[1] = 0;
-      }
+      R.w[0] = p[0];
+      R.w[1] = p[1];
       R.w[2] = p[2];
     }
     const int64_t gi = g_row + kc / G;
@@ -242,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
     }
     const float S = half_bits_to_f32(R.s16);
     const float Z = ASYM ? half_bits_to_f32(R.z16) : (float)(1 << (BITS - 1));
-    const int hi_base = TL::kCodes == 32 ? 0 : 8 * ((kb / 16 + b_half) & 1);
+    const int pair_base = TL::kCodes == 32 ? 0 : 8 * ((kb / 16 + b_half) & 1);
     constexpr int kPairs = TL::kCodes / 2;
     uint32_t hi[kPairs], lo[kPairs];
     if constexpr (kSplit) {
@@ -253,14 +248,14 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
           r0 = 1.0f / RA.sv[t >> 1][2 * (t & 1)];
           r1 = 1.0f / RA.sv[t >> 1][2 * (t & 1) + 1];
         }
-        dequant_pair_split<kScaleB>(code_pair<BITS>(R.w, t, hi_base), Z, S, r0, r1, hi[t], lo[t]);
+        dequant_pair_split<kScaleB>(code_pair<BITS>(R.w, t, pair_base), Z, S, r0, r1, hi[t], lo[t]);
       }
     } else {
       const uint32_t zh = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(1024.0f + Z));
       const uint32_t zmagic2 = zh | (zh << 16);
       const uint32_t s2 = (uint32_t)R.s16 | ((uint32_t)R.s16 << 16);
 #pragma unroll
-      for (int t = 0; t < kPairs; ++t) hi[t] = dequant_pair_f16(code_pair<BITS>(R.w, t, hi_base), zmagic2, s2);
+      for (int t = 0; t < kPairs; ++t) hi[t] = dequant_pair_f16(code_pair<BITS>(R.w, t, pair_base), zmagic2, s2);
     }
 #pragma unroll
     for (int q = 0; q < kPairs / 4; ++q) {

@@ -22,7 +22,7 @@
 //   * B fragments never touch LDS: inside one 64-wide K block, lane half h
 //     supplies K offsets [32 h, 32 h + 32) over the four MFMA steps (step s:
 //     32 h + 8 s + j), A fragments are read with the same mapping, and a
-//     lane's B data for the block is one 16-byte chunk of layout v1 whose
+//     lane's B data for the block is one 16-byte chunk of layout v2 whose
 //     code word s holds the 8 offsets of step s.  Each pair is widened
 //     exactly, (1024 + u) - (1024 + Z), and multiplied by S once.
 //   * The tile's scales and zero points are staged in LDS once (K / G <= 64

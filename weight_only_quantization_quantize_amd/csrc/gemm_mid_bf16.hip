@@ -26,7 +26,7 @@
 // B[8(l/32)+j][n = l%32] and holds C[m = 8(v/4) + 4(l/32) + v%4][n = l%32]
 // in accumulator v = 0..15.  Inside one 64-wide K block, lane half h supplies
 // the K offsets [32 h, 32 h + 32) over the four MFMA steps (step s:
-// 32 h + 8 s + j); a lane's B data for the block is one 16-byte layout-v1 chunk.
+// 32 h + 8 s + j); a lane's B data for the block is one 16-byte layout-v2 chunk.
 #include "woq_device.h"
 #include "woq_internal.h"
 

@@ -17,7 +17,7 @@
 //     steps (step s: offsets 32 h + 8 s .. + 8) instead of the usual 8 h + 16 s
 //     ordering; A fragments are read with the same mapping, so each step still
 //     sums every K offset exactly once.  With that order a lane's B data for
-//     the whole block is one 16-byte chunk of layout v1 (32 codes of one
+//     the whole block is one 16-byte chunk of layout v2 (32 codes of one
 //     output column, inside one group since G % 32 == 0), and the code word s
 //     of the chunk holds exactly the 8 K offsets of step s, as the pairs
 //     (w >> 4t) & 0x000F000F, t = 0..3.

@@ -24,7 +24,7 @@
 // K order inside a block.  Lane (r, q) (r = lane % 16, q = lane / 16) supplies
 // at MFMA step s the 8 slots of K offsets 32 q + 8 s + j (j = 0..7) for both
 // A and B, so each slot is summed once and a lane's codes of the block are one
-// 16-byte chunk of layout v1, word s holding step s.
+// 16-byte chunk of layout v2, word s holding step s.
 //
 // Loads.  Codes and X are read in row-contiguous runs (a load never splits a
 // row's segment over lanes of different rows) and turned into MFMA fragments

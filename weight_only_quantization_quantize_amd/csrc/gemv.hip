@@ -25,8 +25,8 @@
 // subnormals of value u * 2^-24 (resp. 16u * 2^-24), which v_dot2 multiplies
 // exactly; one AND per pair and
 //   sum x (u - Z) = 2^24 (a + b / 16) - Z * sum x.
-// 3-bit codes are dotted in two parts, u = lo + 4 hi, each masked where it
-// sits (partial sums of known power-of-two weight) instead of reassembled.  bf16 activations
+// 3-bit codes (layout v2: each pair's three bits together) are masked where
+// they sit, as subnormals of weight 1, 8 or 64.  bf16 activations
 // OR the pair into the 16-bit float MAGIC + u (0x4300 = 128) and remove
 // (MAGIC + Z) * sum x instead.
 //
@@ -114,31 +114,26 @@ __device__ inline float chunk_dot(const Codes<BITS>& c, const uint32_t (&xr)[16]
       for (int t = 0; t < 4; ++t) a = XT::dot2(((c.w[j] >> (4 * t)) & 0x000F000Fu) | magic, xr[4 * j + t], a);
     return a - (XT::kMagic + Z) * (xs.part[0] + xs.part[1]);
   } else if constexpr (kF16) {
-    // u = lo + 4 hi, each part dotted where it sits in its word, as fp16
-    // subnormals of a known power-of-two weight (one AND and one dot2 per
-    // masked pair, no bit moves): the low pairs t = 2q, 2q + 1 of word
-    // w_(t/8) are (w >> 4q) & 0x00030003 (weight 1) and & 0x000C000C
-    // (weight 4); the high bit of pair t = 4q + j is (w2 >> 4q) & (0x00010001
-    // << j) (weight 2^j).
-    float l0 = 0.0f, l1 = 0.0f, h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // Layout v2 keeps each pair's three bits together, so a masked pair is
+    // read where it sits as two fp16 subnormals of a known power-of-two
+    // weight (one AND and one dot2 per pair): fields j = 0, 1, 2 of word w
+    // (pair 5w + j, bits 3j) weigh 1, 8, 64; after w >> 9, fields j = 3, 4
+    // weigh 1, 8, and bit 6 of each half holds bit w of pair 15's codes,
+    // which three masks and two shift-ORs assemble at bits 6..8 (weight 64).
+    float a[3] = {0.0f, 0.0f, 0.0f};
+    uint32_t hi[3];
 #pragma unroll
-    for (int wi = 0; wi < 2; ++wi) {
-      const uint32_t w = wi ? c.w1 : c.w0;
+    for (int wi = 0; wi < 3; ++wi) {
+      const uint32_t w = wi == 0 ? c.w0 : (wi == 1 ? c.w1 : c.w2);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t ws = w >> (4 * q);
-        l0 = XT::dot2(ws & 0x00030003u, xr[8 * wi + 2 * q], l0);
-        l1 = XT::dot2(ws & 0x000C000Cu, xr[8 * wi + 2 * q + 1], l1);
-      }
+      for (int j = 0; j < 3; ++j) a[j] = XT::dot2(w & (0x00070007u << (3 * j)), xr[5 * wi + j], a[j]);
+      hi[wi] = w >> 9;
+      a[0] = XT::dot2(hi[wi] & 0x00070007u, xr[5 * wi + 3], a[0]);
+      a[1] = XT::dot2(hi[wi] & 0x00380038u, xr[5 * wi + 4], a[1]);
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t ws = c.w2 >> (4 * q);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) h[j] = XT::dot2(ws & (0x00010001u << j), xr[4 * q + j], h[j]);
-    }
-    const float a = l0 + 0.25f * l1 + 4.0f * h[0] + 2.0f * h[1] + h[2] + 0.5f * h[3];
-    return 16777216.0f * a - Z * (xs.part[0] + xs.part[1]);
+    const uint32_t p15 = (((((hi[2] & 0x00400040u) << 1) | (hi[1] & 0x00400040u)) << 1)) | (hi[0] & 0x00400040u);
+    a[2] = XT::dot2(p15, xr[15], a[2]);
+    return 16777216.0f * (a[0] + 0.125f * a[1] + 0.015625f * a[2]) - Z * (xs.part[0] + xs.part[1]);
   } else {
     float a = 0.0f;
 #pragma unroll

@@ -1,4 +1,4 @@
-// GPTQ on the GPU, writing layout v1.
+// GPTQ on the GPU, writing layout v2.
 //
 // What is computed ("CMU 11-868 L19-L20 Model Quantization", section "The
 // algorithm in four steps"; the layer-wise objective of "Quantising Large
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(256) void wide_group_params_kernel(const double* __
 // err * U[c][j] from its 16 columns.  Columns j < c see U[c][j] = 0 and
 // column c itself becomes w_hat, neither of which is read again.  Group
 // statistics (group size 32 or 64) combine eight per-wave partials in a
-// fixed order.  Writes the codes (layout v1), the parameters of the groups
+// fixed order.  Writes the codes (layout v2), the parameters of the groups
 // that start in the block and the scaled errors Et[c][n].
 constexpr int kBlockWaves = 8;
 constexpr int kOwn = kColBlock / kBlockWaves;

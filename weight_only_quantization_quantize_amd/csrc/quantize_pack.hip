@@ -1,4 +1,4 @@
-// Group-wise RTN quantization of fp16 weights into layout-v1 codes plus fp16
+// Group-wise RTN quantization of fp16 weights into layout-v2 codes plus fp16
 // scales / zero points, bit-exact with the reference definition:
 //
 //   w = fl32(W * s)                       (optional AWQ fold, one multiply)

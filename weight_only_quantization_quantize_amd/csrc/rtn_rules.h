@@ -2,7 +2,7 @@
 // group scale / zero point and the code of one weight, each decision one
 // correctly rounded binary32 operation (IEEE division or its exact
 // equivalent, rintf = round half to even, fp32 -> fp16 round-to-nearest-even
-// with subnormals), and the layout-v1 store of a 32-code chunk.
+// with subnormals), and the layout-v2 store of a 32-code chunk.
 //
 //   symmetric : S = f16(max|w| / (2^(b-1)-1)), u = clip(rne(w/S), -2^(b-1), 2^(b-1)-1) + 2^(b-1)
 //   asymmetric: r = max-min (1 if 0), S = f16(r / (2^b-1)),
@@ -114,18 +114,23 @@ __device__ inline void store_chunk(uint8_t* __restrict__ packed, int64_t n, int 
     }
     *reinterpret_cast<u32x4_t*>(packed + n * (int64_t)(K / 2) + (int64_t)kc * 16) = out;
   } else {
-    uint32_t w0 = 0, w1 = 0, w2 = 0;
+    // layout v2: pair t < 15 whole at bits 16 h + 3 (t % 5) of word t / 5;
+    // pair 15's bit b at bit 16 h + 15 of word b
+    uint32_t w[3] = {0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const int t = i >> 1, h = i & 1;
-      const uint32_t lo = (u[i] & 3u) << (16 * h + 2 * (t & 7));
-      if (t < 8) w0 |= lo; else w1 |= lo;
-      w2 |= ((u[i] >> 2) & 1u) << (16 * h + t);
+      if (t < 15) {
+        w[t / 5] |= (u[i] & 7u) << (16 * h + 3 * (t % 5));
+      } else {
+#pragma unroll
+        for (int b = 0; b < 3; ++b) w[b] |= ((u[i] >> b) & 1u) << (16 * h + 15);
+      }
     }
     uint32_t* dst = reinterpret_cast<uint32_t*>(packed + n * (int64_t)(3 * K / 8) + (int64_t)kc * 12);
-    dst[0] = w0;
-    dst[1] = w1;
-    dst[2] = w2;
+    dst[0] = w[0];
+    dst[1] = w[1];
+    dst[2] = w[2];
   }
 }
 

@@ -130,7 +130,7 @@ woq_status check_gptq(int64_t T, int64_t N, int64_t K, int32_t bits, int32_t gro
 
 extern "C" {
 
-int32_t woq_layout_version(void) { return WOQ_LAYOUT_V1; }
+int32_t woq_layout_version(void) { return WOQ_LAYOUT_V2; }
 
 size_t woq_packed_bytes(int64_t N, int64_t K, int32_t bits) {
   if ((bits != 3 && bits != 4) || N < 1 || K < 32 || K % 32 != 0) return 0;

@@ -61,7 +61,7 @@ struct BF16 {
 };
 
 // ---------------------------------------------------------------------------
-// Layout-v1 decode.  Each helper returns the code pair (k, k+1) of pair index
+// Packed-code decode.  Each helper returns the code pair (k, k+1) of pair index
 // t in the two 16-bit halves, OR-ed with the magic pattern.
 // ---------------------------------------------------------------------------
 
@@ -79,14 +79,15 @@ __device__ inline uint32_t pair4(uint32_t w, int t, uint32_t magic2) {
   return ((w >> (4 * t)) & 0x000F000Fu) | magic2;
 }
 
-// 3-bit unit (w0, w1, w2) holding 32 k: pair t (0..15): low two bits in
-// w_(t/8) at [2(t%8), +2) and [16 + 2(t%8), +2); high bit in w2 at t and 16+t.
+// 3-bit unit (w0, w1, w2) holding 32 k, layout v2: pair t < 15 is the 3-bit
+// field at bits [3 (t % 5), +3) and [16 + 3 (t % 5), +3) of word w_(t / 5);
+// pair 15 keeps bit b of each half's code at bit 15 / 31 of word w_b.
 __device__ inline uint32_t pair3(uint32_t w0, uint32_t w1, uint32_t w2, int t, uint32_t magic2) {
-  const uint32_t lw = (t < 8) ? w0 : w1;
-  const int tt = t & 7;
-  const uint32_t lo = (lw >> (2 * tt)) & 0x00030003u;
-  const uint32_t hi = ((w2 >> t) & 0x00010001u) << 2;
-  return lo | hi | magic2;
+  if (t < 15) {
+    const uint32_t w = t < 5 ? w0 : (t < 10 ? w1 : w2);
+    return ((w >> (3 * (t % 5))) & 0x00070007u) | magic2;
+  }
+  return ((w0 >> 15) & 0x00010001u) | ((w1 >> 14) & 0x00020002u) | ((w2 >> 13) & 0x00040004u) | magic2;
 }
 
 // Sum over a team of `team` consecutive lanes (team a power of two <= 64);

@@ -88,7 +88,7 @@ hipError_t awq_noalloc_scratch(void** ptr);
 hipError_t launch_dense_ref(const void* A, const void* B, int64_t M, int64_t N, int64_t K, float* Y,
                             hipStream_t stream);
 
-// GPTQ into layout v1 (scratch in the caller's workspace).
+// GPTQ into layout v2 (scratch in the caller's workspace).
 size_t gptq_workspace_bytes(int64_t T, int64_t N, int64_t K);
 hipError_t launch_gptq(const void* X, const void* W, int64_t T, int64_t N, int64_t K, int bits, int group_size,
                        bool asymmetric, double damp, void* packed, void* scales, void* zeros, void* workspace,

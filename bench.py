@@ -82,6 +82,8 @@ def parse():
     p.add_argument("--write-traffic", default=None, metavar="DIR",
                    help="write profiles/gemv_traffic.json from rocprofv3 counter CSVs in DIR and exit")
     p.add_argument("--copy-mib", type=int, default=256, help="size of the --copy-calibration run used for DIR")
+    p.add_argument("--write-trace", default=None, metavar="DIR",
+                   help="write profiles/gemv_trace.json from the rocprofv3 kernel_trace.csv under DIR and exit")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (for HBM counter calibration) and exit")
     p.add_argument("--gemm-only", default=None, metavar="M,N,K",
@@ -111,29 +113,86 @@ class Timer:
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
 
 
+def trace_entry(nb):
+    """The committed kernel trace's statistics of the same GEMV (mean, median,
+    min per dispatch) and the fraction of peak its mean gives; None when the
+    GEMV source changed since the trace."""
+    t = measured_trace()
+    if t is None:
+        return None
+    return {"mean_us": t["mean_us"], "median_us": t["median_us"], "min_us": t["min_us"],
+            "dispatches": t["dispatches"], "frac_from_mean": round(nb / (t["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "source": "profiles/gemv_trace.json (rocprofv3 --kernel-trace of bench.py)"}
+
+
 def measured_traffic():
     """HBM bytes per GEMV launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE runs (scaled by a plain-copy calibration), or None when the
     GEMV source has changed since those counters were taken."""
-    import hashlib
-
     path = os.path.join(ROOT, "profiles", "gemv_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    src = os.path.join(ROOT, "weight_only_quantization_quantize_amd", "csrc", "gemv.hip")
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != t.get("kernel_source_sha256"):
-            return None
+    if gemv_source_sha() != t.get("kernel_source_sha256"):
+        return None
     return int(t["bytes_per_launch"])
+
+
+GEMV_C2_KERNEL = "gemv_kernel<4, true, woq::F16, false, 4, 4, 2>"
+
+
+def gemv_source_sha():
+    import hashlib
+
+    with open(os.path.join(ROOT, "weight_only_quantization_quantize_amd", "csrc", "gemv.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_trace():
+    """Per-dispatch duration statistics of the K = N = 8192 GEMV from the
+    committed rocprofv3 kernel trace of a bench run, or None when the GEMV
+    source has changed since that trace was taken."""
+    path = os.path.join(ROOT, "profiles", "gemv_trace.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    return t if t.get("kernel_source_sha256") == gemv_source_sha() else None
+
+
+def write_trace(prof_dir):
+    """profiles/gemv_trace.json from the kernel_trace.csv of a rocprofv3
+    --kernel-trace run of bench.py: durations of the dispatches of the
+    K = N = 8192 GEMV instance with its 1024 x 512-thread grid."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(prof_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one kernel_trace.csv under {prof_dir}, found {files}")
+    durs = []
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            grid = int(r.get("Grid_Size_X", r.get("Grid_Size", 0)))
+            if GEMV_C2_KERNEL in r["Kernel_Name"] and grid == 1024 * 512:
+                durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if not durs:
+        raise SystemExit("no K = N = 8192 GEMV dispatches in the trace")
+    d = np.array(durs)
+    out = {"kernel": GEMV_C2_KERNEL, "grid": "1024 x 512 threads", "dispatches": int(d.size),
+           "mean_us": round(float(d.mean()), 3), "median_us": round(float(np.median(d)), 3),
+           "min_us": round(float(d.min()), 3), "max_us": round(float(d.max()), 3),
+           "kernel_source_sha256": gemv_source_sha()}
+    with open(os.path.join(ROOT, "profiles", "gemv_trace.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def write_traffic(prof_dir, copy_mib):
     """Scale the GEMV's FETCH_SIZE / WRITE_SIZE (KiB per dispatch, median) by
     what the same counters read for a plain device copy of copy_mib MiB."""
     import csv
-    import hashlib
 
     def per_kernel(name):
         d = {}
@@ -157,12 +216,11 @@ def write_traffic(prof_dir, copy_mib):
             continue
         fk, wk = float(np.median(fetch[k])), float(np.median(write.get(k, [0.0])))
         table.append((k, len(fetch[k]), fk, wk, fk * fetch_scale * 1024, wk * write_scale * 1024))
-    gemv = [t for t in table if "gemv_kernel<4, true, woq::F16, false, 4, 4, 2>" in t[0]]
+    gemv = [t for t in table if GEMV_C2_KERNEL in t[0]]
     if len(gemv) != 1:
         raise SystemExit("the K = N = 8192 GEMV kernel is not in the counter CSVs")
     k, _, fk, wk, rb, wb = gemv[0]
-    with open(os.path.join(ROOT, "weight_only_quantization_quantize_amd", "csrc", "gemv.hip"), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    sha = gemv_source_sha()
     out = {
         "kernel": "gemv_kernel<4, true, F16, false, 4, 4, 2>",
         "workload": "M=1 K=8192 N=8192 4-bit asym g128",
@@ -606,6 +664,9 @@ def main():
     if args.write_traffic:
         write_traffic(args.write_traffic, args.copy_mib)
         return
+    if args.write_trace:
+        write_trace(args.write_trace)
+        return
 
     import torch
 
@@ -723,6 +784,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac_statistic": f"mean GEMV duration from HIP events on the launch stream around each step's burst "
+                              f"of {GEMV_BURST} back-to-back launches (inter-kernel gaps included)",
+            "trace": trace_entry(nb),
             "traffic": measured_traffic(),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "bytes_per_launch": nb,

@@ -139,7 +139,7 @@ def measured_traffic():
     return int(t["bytes_per_launch"])
 
 
-GEMV_C2_KERNEL = "gemv_kernel<4, true, woq::F16, false, 4, 4, 2>"
+GEMV_C2_KERNEL = "gemv_kernel<4, true, woq::F16, false, 4, 4, 2, false>"
 
 
 def gemv_source_sha():
@@ -222,7 +222,7 @@ def write_traffic(prof_dir, copy_mib):
     k, _, fk, wk, rb, wb = gemv[0]
     sha = gemv_source_sha()
     out = {
-        "kernel": "gemv_kernel<4, true, F16, false, 4, 4, 2>",
+        "kernel": "gemv_kernel<4, true, F16, false, 4, 4, 2, false>",
         "workload": "M=1 K=8192 N=8192 4-bit asym g128",
         "kernel_source_sha256": sha,
         "fetch_size_kib": fk,
@@ -553,8 +553,77 @@ def time_ceilings(torch, dev):
     fl = 512 * 4 * iters * 4 * 2 * 32 * 32 * 16
     out["mfma_f16_32x32x16_random_operands"] = {
         "us": round(us, 1), "tflops": round(fl / us / 1e6, 1), "frac_mfma": round(fl / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)}
+    out["mfma_valu_coissue"] = time_mfma_valu(torch, dev, lib, stream)
     del bufs
     return out
+
+
+def time_mfma_valu(torch, dev, lib, stream):
+    """Whether VALU work hides under MFMAs on one SIMD, and the clock it runs at:
+    512 workgroups of 4 waves (two per SIMD), 20000 steps of 4 fp16 32x32x16
+    MFMAs and/or 16-64 integer VALU operations per wave (committed probe
+    woq_probe_mfma_valu).  'clock_ghz' is the shader clock counter's rate
+    against the 100 MHz real-time counter, median over workgroups."""
+    from weight_only_quantization_quantize_amd import _lib
+
+    src = torch.randn(1 << 19, device=dev).to(torch.float16)
+    blocks, iters = 512, 20000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(4 * blocks, dtype=torch.int64, device=dev)
+    out = {"blocks": blocks, "waves_per_simd": 2, "iters": iters}
+    for nm, nv in ((4, 0), (4, 16), (4, 32), (4, 64), (0, 32), (0, 64)):
+        def launch():
+            _lib.check(lib.woq_probe_mfma_valu(src.data_ptr(), blocks, iters, nm, nv, sink.data_ptr(),
+                                               clocks.data_ptr(), 0, stream), "woq_probe_mfma_valu")
+        launch()
+        us = burst_us(torch, [launch, launch], reps=2)
+        c = clocks.view(-1, 4).cpu().numpy().astype(np.float64)
+        ghz = float(np.median((c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1) * 0.1))
+        out[f"mfma{nm}_valu{nv}"] = {"us": round(us, 1), "clock_ghz": round(ghz, 3)}
+    t = {k: v["us"] for k, v in out.items() if isinstance(v, dict)}
+    for nv in (32, 64):
+        mixed, m, v = t[f"mfma4_valu{nv}"], t["mfma4_valu0"], t[f"mfma0_valu{nv}"]
+        out[f"valu{nv}_overlap"] = {"mixed_over_max": round(mixed / max(m, v), 3),
+                                    "mixed_over_sum": round(mixed / (m + v), 3)}
+    return out
+
+
+def time_gemv_timeline(torch, dev, lib, stream, x, sets, N, y):
+    """Per-wave timeline of the K = N = 8192 decode GEMV (the library kernel's
+    own instance with timeline stamps, committed probe woq_probe_gemv_timeline):
+    a burst of 32 back-to-back launches over the rotated packed sets; medians
+    over launches 8..31 of the launch span (first wave start to last wave
+    end), the idle gap before the next launch, and per-wave times from the
+    launch's first start, in us (100 MHz counter: 0.01 us resolution)."""
+    from weight_only_quantization_quantize_amd import _lib
+
+    words = int(lib.woq_probe_gemv_timeline_words(N))
+    L, R = 32, len(sets)
+    tl = torch.zeros(L, words, dtype=torch.int64, device=dev)
+
+    def launch(j):
+        p, s, z = sets[j % R]
+        _lib.check(lib.woq_probe_gemv_timeline(x.data_ptr(), p.data_ptr(), s.data_ptr(), z.data_ptr(), N,
+                                               y.data_ptr(), tl[j].data_ptr(), words, stream),
+                   "woq_probe_gemv_timeline")
+    burst_us(torch, [lambda j=j: launch(j) for j in range(L)], reps=1)
+    T = tl.view(L, -1, 8).cpu().numpy().astype(np.float64) / 100.0   # us
+    span, gap, xr, first, end = [], [], [], [], []
+    for j in range(8, L):
+        t = T[j]
+        t0 = t[:, 0].min()
+        span.append(t[:, 4].max() - t0)
+        if j + 1 < L:
+            gap.append(T[j + 1][:, 0].min() - t[:, 4].max())
+        xr.append(np.percentile(t[:, 1] - t[:, 0], [10, 50, 90]))
+        first.append(np.percentile(t[:, 2] - t0, [10, 50, 90]))
+        end.append(np.percentile(t[:, 4] - t0, [10, 50, 90]))
+    med = lambda a: [round(float(v), 2) for v in np.median(np.array(a), axis=0)]
+    return {"waves": int(T.shape[1]), "launches": L - 8,
+            "span_us": round(float(np.median(span)), 2), "gap_to_next_launch_us": round(float(np.median(gap)), 2),
+            "x_staged_after_start_us_p10_p50_p90": med(xr),
+            "first_step_done_us_p10_p50_p90": med(first),
+            "wave_end_us_p10_p50_p90": med(end)}
 
 
 def row_checks(checks, rows):
@@ -797,6 +866,8 @@ def main():
     if not args.no_rows:
         del Ws, W0
         result["rows"] = time_rows(torch, ops, synth, checks)
+        result["rows"]["gemv_timeline_k8192_n8192"] = time_gemv_timeline(
+            torch, dev, _lib.load(), torch.cuda.current_stream().cuda_stream, x, sets, N, y)
 
     if not args.no_cpu_baseline:
         ops.gemv(x, *sets[0], N, K, bits, G, out=y)

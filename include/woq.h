@@ -125,8 +125,10 @@ woq_status woq_quantize_pack(const void* W, const float* act_scale, int64_t N, i
  *   act_scale : fp32 [K] (the same s given to woq_quantize_pack) or NULL
  *   packed, scales, zeros : as written by woq_quantize_pack
  *   y         : out, [N] of xdtype
- * Accumulates in fp32.  x / s is rounded once to xdtype before use; the
- * integer (u - Z) is multiplied exactly and S is applied in fp32 per group. */
+ * Accumulates in fp32.  x * r(s) (r(s): the hardware reciprocal, within
+ * 1 ulp of 1 / s) is rounded once to xdtype before use (a bf16 pair hi + lo
+ * for bf16 x); the integer (u - Z) is multiplied exactly and S is applied in
+ * fp32 per group. */
 woq_status woq_w4a16_gemv(const void* x, int32_t xdtype, const float* act_scale,
                           const void* packed, const void* scales, const void* zeros,
                           int64_t N, int64_t K, int32_t bits, int32_t group_size, int32_t asymmetric,
@@ -140,8 +142,9 @@ woq_status woq_w4a16_gemv(const void* x, int32_t xdtype, const float* act_scale,
  * (always above 64 rows; at 33..64 rows when N >= 16384 or the small-batch
  * kernel does not take the shape), feed MFMA with dequantized weights: for
  * fp16, w_hat rounded once to fp16 (decoded straight into operand registers
- * for 4-bit codes, or staged in LDS) with X * fl32(1 / s) rounded once to
- * fp16; for bf16, X used as given and w_hat * fl32(1 / s) kept as a bf16 pair
+ * for 4-bit codes, or staged in LDS) with X * r(s) rounded once to fp16
+ * (r(s): the hardware reciprocal, within 1 ulp of 1 / s); for bf16, X used
+ * as given and w_hat * r(s) kept as a bf16 pair
  * hi + lo (about 16 significant bits), or, for bf16 X at 33..127 rows without
  * an AWQ scale (group size a power of two >= 64), the exact 128 + u with the
  * scale applied per group in fp32.  fp32 accumulation throughout; the
@@ -259,12 +262,34 @@ woq_status woq_gptq_quantize_pack(const void* X, const void* W, int64_t T, int64
  *   flop each) on operands read from src (device, at least 1 MiB of fp16
  *   data, 16-byte aligned); the sums go to sink (device, blocks * 256 floats)
  *   only when store != 0.
+ * woq_probe_mfma_valu: whether VALU work hides under MFMAs, and the clock
+ *   the SIMDs run at.  blocks workgroups of 4 waves, each running `iters`
+ *   steps of mfma_per_iter v_mfma_f32_32x32x16_f16 (4 independent chains)
+ *   and valu_per_iter independent 32-bit integer VALU operations;
+ *   (mfma_per_iter, valu_per_iter) is (4, 0|16|32|64) or (0, 32|64).  src
+ *   and sink as for woq_probe_mfma_rate.  Wave 0 of workgroup b writes the
+ *   shader clock counter (s_memtime) at its start and end to clocks[4b] and
+ *   clocks[4b + 1], and the 100 MHz real-time counter (s_memrealtime) to
+ *   clocks[4b + 2] and clocks[4b + 3] (device, 4 * blocks uint64).
+ * woq_probe_gemv_timeline: the decode GEMV (woq_w4a16_gemv with K = 8192,
+ *   group 128, 4-bit asymmetric codes, fp16 x, no activation scale; N rows,
+ *   the same launch shape and result y) with a per-wave timeline: 8 uint64
+ *   words per wave in timeline (device), the 100 MHz real-time counter at the
+ *   wave's start, after x is staged, after its first row step, after the
+ *   stream, and at its end, then the XCD id and two zero words.
+ *   timeline_words must be at least woq_probe_gemv_timeline_words(N) (0 for
+ *   N outside [1, 2^31]).
  * Asynchronous on stream; invalid arguments return WOQ_ERR_INVALID_ARGUMENT. */
 woq_status woq_probe_stream_read(const void* p, size_t bytes, int32_t blocks, int32_t threads, int32_t unroll,
                                  void* sink, int32_t store, void* stream);
 woq_status woq_probe_empty(int32_t blocks, int32_t threads, void* stream);
 woq_status woq_probe_mfma_rate(const void* src, int32_t blocks, int32_t iters, float* sink, int32_t store,
                                void* stream);
+woq_status woq_probe_mfma_valu(const void* src, int32_t blocks, int32_t iters, int32_t mfma_per_iter,
+                               int32_t valu_per_iter, float* sink, uint64_t* clocks, int32_t store, void* stream);
+size_t woq_probe_gemv_timeline_words(int64_t N);
+woq_status woq_probe_gemv_timeline(const void* x, const void* packed, const void* scales, const void* zeros,
+                                   int64_t N, void* y, uint64_t* timeline, size_t timeline_words, void* stream);
 
 /* Static text for a status code. */
 const char* woq_status_string(woq_status status);

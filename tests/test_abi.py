@@ -301,6 +301,19 @@ def test_hip_error_surfaces_without_a_device(lib):
         (lambda l: l.woq_probe_mfma_rate(FAKE, 0, 10, FAKE, 0, None), "blocks must be"),
         (lambda l: l.woq_probe_mfma_rate(FAKE, 4, 0, FAKE, 0, None), "iters must be"),
         (lambda l: l.woq_probe_mfma_rate(FAKE, 4, 10, None, 0, None), "sink must be"),
+        (lambda l: l.woq_probe_mfma_valu(None, 4, 10, 4, 0, FAKE, FAKE, 0, None), "src must be"),
+        (lambda l: l.woq_probe_mfma_valu(FAKE, 0, 10, 4, 0, FAKE, FAKE, 0, None), "blocks must be"),
+        (lambda l: l.woq_probe_mfma_valu(FAKE, 4, 0, 4, 0, FAKE, FAKE, 0, None), "iters must be"),
+        (lambda l: l.woq_probe_mfma_valu(FAKE, 4, 10, 4, 8, FAKE, FAKE, 0, None), "(mfma_per_iter, valu_per_iter)"),
+        (lambda l: l.woq_probe_mfma_valu(FAKE, 4, 10, 0, 0, FAKE, FAKE, 0, None), "(mfma_per_iter, valu_per_iter)"),
+        (lambda l: l.woq_probe_mfma_valu(FAKE, 4, 10, 4, 0, None, FAKE, 0, None), "sink must be"),
+        (lambda l: l.woq_probe_mfma_valu(FAKE, 4, 10, 4, 0, FAKE, None, 0, None), "clocks must be"),
+        (lambda l: l.woq_probe_mfma_valu(FAKE, 4, 10, 4, 0, FAKE, FAKE + 4, 0, None), "clocks must be"),
+        (lambda l: l.woq_probe_gemv_timeline(FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1 << 20, None), "N must be"),
+        (lambda l: l.woq_probe_gemv_timeline(None, FAKE, FAKE, FAKE, 8192, FAKE, FAKE, 1 << 20, None), "x must be"),
+        (lambda l: l.woq_probe_gemv_timeline(FAKE, FAKE, FAKE, None, 8192, FAKE, FAKE, 1 << 20, None), "zeros must be"),
+        (lambda l: l.woq_probe_gemv_timeline(FAKE, FAKE, FAKE, FAKE, 8192, FAKE, None, 1 << 20, None), "timeline must be"),
+        (lambda l: l.woq_probe_gemv_timeline(FAKE, FAKE, FAKE, FAKE, 8192, FAKE, FAKE, 100, None), "timeline too small"),
     ],
 )
 def test_probes_reject(lib, call, needle):

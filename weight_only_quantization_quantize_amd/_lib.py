@@ -45,6 +45,9 @@ SIGNATURES = {
     "woq_probe_stream_read": (_i32, [_vp, _sz, _i32, _i32, _i32, _vp, _i32, _vp]),
     "woq_probe_empty": (_i32, [_i32, _i32, _vp]),
     "woq_probe_mfma_rate": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp]),
+    "woq_probe_mfma_valu": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp]),
+    "woq_probe_gemv_timeline_words": (_sz, [_i64]),
+    "woq_probe_gemv_timeline": (_i32, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "woq_status_string": (ctypes.c_char_p, [_i32]),
     "woq_last_error": (ctypes.c_char_p, []),
 }

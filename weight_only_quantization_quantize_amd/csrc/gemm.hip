@@ -235,8 +235,8 @@ __global__ __launch_bounds__(kThreads * NS) void gemm_direct_kernel(
         for (int e = 0; e < 4; ++e) {
           const float d0 = e < 2 ? s0[2 * e] : s1[2 * e - 4];
           const float d1 = e < 2 ? s0[2 * e + 1] : s1[2 * e - 3];
-          const float a0 = XT::to_f32((uint16_t)(v[e] & 0xFFFFu)) / d0;
-          const float a1 = XT::to_f32((uint16_t)(v[e] >> 16)) / d1;
+          const float a0 = XT::to_f32((uint16_t)(v[e] & 0xFFFFu)) * act_recip(d0);
+          const float a1 = XT::to_f32((uint16_t)(v[e] >> 16)) * act_recip(d1);
           const uint16_t h0 = XT::from_f32(a0), h1 = XT::from_f32(a1);
           v[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
           if (kSplitX)

@@ -13,10 +13,10 @@
 // accumulators per lane; two waves per SIMD hide each other's waits).  The K
 // loop advances BK (64 for fp16, 32 for bf16) at a time through a
 // double-buffered LDS stage holding
-//   A: X[m0:m0+256, k:k+BK] (for fp16 with an AWQ scale, x * fl32(1 / s)
+//   A: X[m0:m0+256, k:k+BK] (for fp16 with an AWQ scale, x * act_recip(s)
 //      rounded once),
 //   B: w_hat[n0:n0+256, k:k+BK] = (u - Z) * S rounded to the activation type
-//      (for bf16 with an AWQ scale, (u - Z) * S * fl32(1 / s)),
+//      (for bf16 with an AWQ scale, (u - Z) * S * act_recip(s)),
 // decoded once per workgroup from the packed codes: thread t owns half of
 // column n0 + t/2 (BK/2 codes, which never cross a group since G % 32 == 0)
 // and its (S, Z).  The code pair is widened exactly, (1024 + u) - (1024 + Z) =
@@ -163,8 +163,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
   const int64_t g_row = (int64_t)b_col * gpr;
   const uint32_t b_dst = (uint32_t)(2 * kStage + b_lcol * LD + (BK / 2) * b_half);
 
-  // With an AWQ scale, fp16 stages x * fl32(1 / s) in A; bf16 keeps X exact
-  // and folds fl32(1 / s) into the split weight instead, since rounding x / s
+  // With an AWQ scale, fp16 stages x * act_recip(s) in A; bf16 keeps X exact
+  // and folds act_recip(s) into the split weight instead, since rounding x / s
   // to 8 significant bits would dominate the error when a few scaled channels
   // carry the output.
   constexpr bool kScaleA = SCALE && !kSplit, kScaleB = SCALE && kSplit;
@@ -218,8 +218,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
       const float4_t s1 = *reinterpret_cast<const float4_t*>(s + kb + 8 * a_seg + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        inv[e] = 1.0f / s0[e];
-        inv[e + 4] = 1.0f / s1[e];
+        inv[e] = act_recip(s0[e]);
+        inv[e + 4] = act_recip(s1[e]);
       }
     }
 #pragma unroll
@@ -245,8 +245,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds_kernel(
       for (int t = 0; t < kPairs; ++t) {
         float r0 = 1.0f, r1 = 1.0f;
         if constexpr (kScaleB) {
-          r0 = 1.0f / RA.sv[t >> 1][2 * (t & 1)];
-          r1 = 1.0f / RA.sv[t >> 1][2 * (t & 1) + 1];
+          r0 = act_recip(RA.sv[t >> 1][2 * (t & 1)]);
+          r1 = act_recip(RA.sv[t >> 1][2 * (t & 1) + 1]);
         }
         dequant_pair_split<kScaleB>(code_pair<BITS>(R.w, t, pair_base), Z, S, r0, r1, hi[t], lo[t]);
       }

@@ -179,8 +179,8 @@ __global__ __launch_bounds__(kThreads, kRing == 3 ? 2 : 1) void gemm_mid_kernel(
       const float4_t s1 = *reinterpret_cast<const float4_t*>(s + kb + 8 * a_seg + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        inv[e] = 1.0f / s0[e];
-        inv[e + 4] = 1.0f / s1[e];
+        inv[e] = act_recip(s0[e]);
+        inv[e + 4] = act_recip(s1[e]);
       }
     }
 #pragma unroll

@@ -23,7 +23,7 @@
 //     (w >> 4t) & 0x000F000F, t = 0..3.
 //   * Each pair is widened exactly, (1024 + u) - (1024 + Z) = u - Z in fp16,
 //     and multiplied by S once: the weight is the same fp16 w_hat as in the
-//     LDS-staged kernel.  With an AWQ scale, A holds x * fl32(1 / s) rounded
+//     LDS-staged kernel.  With an AWQ scale, A holds x * act_recip(s) rounded
 //     once to fp16, also as there.
 //
 // The tile's scales and zero points (K / G <= 40 groups) are staged in LDS
@@ -208,8 +208,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
       const float4_t s1 = *reinterpret_cast<const float4_t*>(s + kb + 8 * a_seg + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        inv[e] = 1.0f / s0[e];
-        inv[e + 4] = 1.0f / s1[e];
+        inv[e] = act_recip(s0[e]);
+        inv[e + 4] = act_recip(s1[e]);
       }
     }
 #pragma unroll

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(
   load_sz(tile);
 
   if constexpr (SCALE) {
-    // x' = x / s rounded once to the activation type
+    // x' = x * (1 / s) rounded once to the activation type
 #pragma unroll
     for (int b = 0; b < BPW; ++b)
 #pragma unroll
@@ -160,8 +160,8 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(
           const uint32_t v = a[b][i][e];
           const float d0 = e < 2 ? s0[2 * e] : s1[2 * e - 4];
           const float d1 = e < 2 ? s0[2 * e + 1] : s1[2 * e - 3];
-          const uint16_t h0 = XT::from_f32(XT::to_f32((uint16_t)(v & 0xFFFFu)) / d0);
-          const uint16_t h1 = XT::from_f32(XT::to_f32((uint16_t)(v >> 16)) / d1);
+          const uint16_t h0 = XT::from_f32(XT::to_f32((uint16_t)(v & 0xFFFFu)) * act_recip(d0));
+          const uint16_t h1 = XT::from_f32(XT::to_f32((uint16_t)(v >> 16)) * act_recip(d1));
           a[b][i][e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
         }
       }

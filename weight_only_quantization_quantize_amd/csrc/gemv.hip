@@ -11,8 +11,8 @@
 // 32 weights (one 16-byte / 12-byte load per lane per segment).  A workgroup
 // holds RPB rows x SPR segments, one wave per (row, segment); lane p of the
 // wave for segment g always owns chunk 64 g + p, so its 32 activations are
-// read once (from x / s staged in LDS) and stay in 16 registers (32 for bf16
-// with an AWQ scale, where x / s is kept as a bf16 pair hi + lo).
+// read once (from x' = x / s staged in LDS) and stay in 16 registers (32 for
+// bf16 with an AWQ scale, where x' is kept as a bf16 pair hi + lo).
 //
 // Order of the stream.  Workgroup b handles the row groups b, b + B, b + 2B,
 // ... (B = number of workgroups), so at every step the whole GPU reads one
@@ -173,14 +173,31 @@ struct StepLoads {
 // full), group size 128, RPB = max(1, kTargetWaves / SPR_T) rows per workgroup.  SPR_T == 0
 // is the general path (any K <= 16384 that is a multiple of 32, any group
 // size that is a multiple of 32), with the shape passed at run time.
-template <int BITS, bool ASYM, class XT, bool SCALE, int STEPS, int SPR_T, int PASSES>
+// Timeline stamp (100 MHz real-time counter), ordered after every earlier
+// memory operation of the wave; used only by the TL instance.
+__device__ inline uint64_t tl_stamp() {
+  uint64_t t;
+  asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t)::"memory");
+  return t;
+}
+
+// TL: measurement instance that also writes a per-wave timeline to tl (8
+// words per wave: start, x staged, first step computed, stream done, end,
+// XCD id); the kernel's work is otherwise the same.
+template <int BITS, bool ASYM, class XT, bool SCALE, int STEPS, int SPR_T, int PASSES, bool TL>
 __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__ x, const float* __restrict__ s,
                                                     const uint8_t* __restrict__ packed,
                                                     const uint16_t* __restrict__ scales,
                                                     const uint16_t* __restrict__ zeros, int N, int K_rt, int G_rt,
-                                                    int spr_rt, int rpb_rt, uint16_t* __restrict__ y) {
+                                                    int spr_rt, int rpb_rt, uint16_t* __restrict__ y,
+                                                    uint64_t* __restrict__ tl) {
+  uint64_t t_start = 0, t_x = 0, t_first = 0, t_stream = 0;
+  if constexpr (TL) t_start = tl_stamp();
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   constexpr bool kFixed = SPR_T > 0;
+  // the fixed shapes stage all K / 8 16-byte units of x in PASSES passes
+  static_assert(!kFixed || PASSES * (SPR_T >= kTargetWaves ? 1 : kTargetWaves / SPR_T) * SPR_T * 64 >= 256 * SPR_T,
+                "x staging passes do not cover K");
   // bf16 with an AWQ scale: x / s is staged as a bf16 pair hi + lo (about 16
   // significant bits, a second x region in LDS) and each chunk is dotted with
   // both halves.
@@ -242,7 +259,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
 #pragma unroll
   for (int st = 0; st < kPf && st < STEPS; ++st) issue(st);
 
-  // Stage x' = x / s, rounded once to the activation type, in LDS.
+  // Stage x' = x * (1 / s), rounded once to the activation type, in LDS
+  // (act_recip: an IEEE division per activation, up to 32 per thread at
+  // K = 11008, sat in front of the workgroup's first barrier; LLaMA-2-7B down
+  // projection with AWQ: 10.2 -> 9.0 us).
 #pragma unroll
   for (int it = 0; it < PASSES; ++it) {
     const int i = threadIdx.x + it * nthreads;
@@ -250,8 +270,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
     if (SCALE) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float a0 = XT::to_f32((uint16_t)(v[e] & 0xFFFFu)) / sv[it][e / 2][(2 * e) % 4];
-        const float a1 = XT::to_f32((uint16_t)(v[e] >> 16)) / sv[it][e / 2][(2 * e) % 4 + 1];
+        const float a0 = XT::to_f32((uint16_t)(v[e] & 0xFFFFu)) * act_recip(sv[it][e / 2][(2 * e) % 4]);
+        const float a1 = XT::to_f32((uint16_t)(v[e] >> 16)) * act_recip(sv[it][e / 2][(2 * e) % 4 + 1]);
         const uint16_t h0 = XT::from_f32(a0), h1 = XT::from_f32(a1);
         v[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
         if (kSplitX)
@@ -264,6 +284,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
     if (kSplitX) reinterpret_cast<u32x4_t*>(xlo)[i] = vl;
   }
   __syncthreads();
+  if constexpr (TL) t_x = tl_stamp();
 
   // This lane's 32 activations and their sums (lanes past the row end: 0).
   const uint32_t ones2 = XT::kMagic2 == F16::kMagic2 ? 0x3C003C00u : 0x3F803F80u;
@@ -298,8 +319,12 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
     float d = chunk_dot<BITS, XT>(L[st].c, xr, xs, Z, magic);
     if constexpr (kSplitX) d += chunk_dot<BITS, XT>(L[st].c, xl, xsl, Z, magic);
     part[(st * waves + wave) * 64 + lane] = S * d;
+    if constexpr (TL) {
+      if (st == 0) t_first = tl_stamp();
+    }
   }
   __syncthreads();
+  if constexpr (TL) t_stream = tl_stamp();
 
   // Output o = (step, row slot): the spr * 64 partials of one row.
   for (int o = wave; o < STEPS * rpb; o += waves) {
@@ -310,19 +335,33 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
     const int n = row_first - rr + r + st * row_step;
     if (lane == 63 && n < N) y[n] = XT::from_f32(v);
   }
+  if constexpr (TL) {
+    const uint64_t t_end = tl_stamp();
+    if (lane == 0) {
+      uint64_t* o = tl + ((int64_t)blockIdx.x * waves + wave) * 8;
+      o[0] = t_start;
+      o[1] = t_x;
+      o[2] = t_first;
+      o[3] = t_stream;
+      o[4] = t_end;
+      o[5] = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // HW_REG_XCC_ID
+      o[6] = 0;
+      o[7] = 0;
+    }
+  }
 }
 
-template <int BITS, bool ASYM, class XT, bool SCALE, int STEPS, int SPR_T, int PASSES>
+template <int BITS, bool ASYM, class XT, bool SCALE, int STEPS, int SPR_T, int PASSES, bool TL = false>
 hipError_t launch_kernel(const void* x, const float* s, const void* packed, const void* scales, const void* zeros,
                          int64_t N, int64_t K, int G, int spr, int rpb, int64_t blocks, void* y,
-                         hipStream_t stream) {
+                         hipStream_t stream, uint64_t* tl = nullptr) {
   const int threads = rpb * spr * 64;
   constexpr bool kSplitX = SCALE && XT::kMagic2 == BF16::kMagic2;
   const size_t lds = (size_t)(kSplitX ? 2 : 1) * PASSES * threads * 16 + (size_t)STEPS * (threads / 64) * 64 * 4;
-  hipLaunchKernelGGL((gemv_kernel<BITS, ASYM, XT, SCALE, STEPS, SPR_T, PASSES>), dim3((unsigned)blocks), dim3(threads), lds,
+  hipLaunchKernelGGL((gemv_kernel<BITS, ASYM, XT, SCALE, STEPS, SPR_T, PASSES, TL>), dim3((unsigned)blocks), dim3(threads), lds,
                      stream, static_cast<const uint16_t*>(x), s, static_cast<const uint8_t*>(packed),
                      static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)N, (int)K, G, spr,
-                     rpb, static_cast<uint16_t*>(y));
+                     rpb, static_cast<uint16_t*>(y), tl);
   return hipGetLastError();
 }
 
@@ -401,6 +440,42 @@ hipError_t launch_asym(const void* x, int xdtype, const float* s, const void* pa
 
 // Largest K the register-resident GEMV handles (8 segments of 64 chunks).
 int gemv_max_k() { return kMaxSegments * 64 * 32; }
+
+namespace {
+// Launch shape of the K = 8192, G = 128 fixed-shape GEMV for N rows (the
+// same rule launch_scale applies).
+constexpr int kTlSpr = 4, kTlRpb = kTargetWaves / kTlSpr;
+int64_t timeline_shape(int64_t N, int& steps) {
+  const int64_t groups = (N + kTlRpb - 1) / kTlRpb;
+  steps = 1;
+  while (steps < kMaxSteps && groups / (2 * steps) >= kTargetBlocks) steps *= 2;
+  return (groups + steps - 1) / steps;
+}
+}  // namespace
+
+size_t gemv_timeline_words(int64_t N) {
+  int steps = 0;
+  return (size_t)timeline_shape(N, steps) * kTlRpb * kTlSpr * 8;
+}
+
+hipError_t launch_gemv_timeline(const void* x, const void* packed, const void* scales, const void* zeros, int64_t N,
+                                void* y, uint64_t* tl, hipStream_t stream) {
+  int steps = 0;
+  const int64_t blocks = timeline_shape(N, steps);
+  switch (steps) {
+    case 1:
+      return launch_kernel<4, true, F16, false, 1, kTlSpr, 2, true>(x, nullptr, packed, scales, zeros, N, 8192, 128,
+                                                                   kTlSpr, kTlRpb, blocks, y, stream, tl);
+    case 2:
+      return launch_kernel<4, true, F16, false, 2, kTlSpr, 2, true>(x, nullptr, packed, scales, zeros, N, 8192, 128,
+                                                                   kTlSpr, kTlRpb, blocks, y, stream, tl);
+    case 4:
+      return launch_kernel<4, true, F16, false, 4, kTlSpr, 2, true>(x, nullptr, packed, scales, zeros, N, 8192, 128,
+                                                                   kTlSpr, kTlRpb, blocks, y, stream, tl);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gemv(const void* x, int xdtype, const float* act_scale, const void* packed, const void* scales,
                        const void* zeros, int64_t N, int64_t K, int bits, int group_size, bool asymmetric, void* y,

@@ -75,7 +75,81 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(const u32x4_t* __restric
   }
 }
 
+// MFMA / VALU co-issue: ITERS steps of NM v_mfma_f32_32x32x16_f16 (NM / 4
+// per chain, 4 independent chains) and NV independent 32-bit integer VALU
+// operations (8 chains of v_xad_u32) per wave.  Wave 0 of each workgroup
+// records the shader clock counter (s_memtime) and the 100 MHz real-time
+// counter (s_memrealtime) at its start and end in clocks[4 * block ..], so
+// the host can derive the clock the SIMDs ran at.
+template <int NM, int NV>
+__global__ __launch_bounds__(256) void mfma_valu_kernel(const u32x4_t* __restrict__ src, int iters,
+                                                        float* __restrict__ sink, uint64_t* __restrict__ clocks,
+                                                        int store) {
+  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  const int lane = threadIdx.x & 63;
+  const int wave = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  u32x4_t a[4], b[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = src[((wave * 8 + j) & 1023) * 64 + lane];
+    b[j] = src[((wave * 8 + 4 + j) & 1023) * 64 + lane];
+  }
+  float16_t acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = float16_t{};
+  uint32_t v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = a[j & 3][j >> 2] + (uint32_t)lane;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < NM; ++j)
+      acc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_vt, a[j & 3]),
+                                                          __builtin_bit_cast(half8_vt, b[j & 3]), acc[j & 3], 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k & 7] = (v[k & 7] ^ 0x9E3779B9u) + (uint32_t)k;
+  }
+  if (store) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum += acc[j][e];
+    uint32_t t = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t ^= v[j];
+    sink[(int64_t)wave * 64 + lane] = sum + (float)t;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    uint64_t* o = clocks + 4 * (int64_t)blockIdx.x;
+    o[0] = c0;
+    o[1] = c1;
+    o[2] = r0;
+    o[3] = r1;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_mfma_valu(const void* src, int blocks, int iters, int mfma_per_iter, int valu_per_iter, float* sink,
+                            uint64_t* clocks, int store, hipStream_t stream) {
+  const u32x4_t* p = static_cast<const u32x4_t*>(src);
+  const dim3 g((unsigned)blocks), t(256);
+#define WOQ_MV(NM, NV)                                                                                  \
+  if (mfma_per_iter == NM && valu_per_iter == NV) {                                                     \
+    hipLaunchKernelGGL((mfma_valu_kernel<NM, NV>), g, t, 0, stream, p, iters, sink, clocks, store);      \
+    return hipGetLastError();                                                                           \
+  }
+  WOQ_MV(4, 0)
+  WOQ_MV(4, 16)
+  WOQ_MV(4, 32)
+  WOQ_MV(4, 64)
+  WOQ_MV(0, 32)
+  WOQ_MV(0, 64)
+#undef WOQ_MV
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_stream_read(const void* p, int64_t bytes, int blocks, int threads, int unroll, void* sink,
                               int store, hipStream_t stream) {

@@ -345,6 +345,47 @@ woq_status woq_probe_mfma_rate(const void* src, int32_t blocks, int32_t iters, f
   WOQ_GUARD_END
 }
 
+woq_status woq_probe_mfma_valu(const void* src, int32_t blocks, int32_t iters, int32_t mfma_per_iter,
+                               int32_t valu_per_iter, float* sink, uint64_t* clocks, int32_t store, void* stream) {
+  WOQ_GUARD_BEGIN
+  if (!src || !aligned(src, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "src must be non-NULL and 16-byte aligned");
+  if (blocks < 1 || blocks > (1 << 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "blocks must be in [1, 65536] (got %d)", blocks);
+  if (iters < 1 || iters > (1 << 24)) return fail(WOQ_ERR_INVALID_ARGUMENT, "iters must be in [1, 2^24] (got %d)", iters);
+  const bool known = (mfma_per_iter == 4 && (valu_per_iter == 0 || valu_per_iter == 16 || valu_per_iter == 32 ||
+                                             valu_per_iter == 64)) ||
+                     (mfma_per_iter == 0 && (valu_per_iter == 32 || valu_per_iter == 64));
+  if (!known)
+    return fail(WOQ_ERR_INVALID_ARGUMENT,
+                "(mfma_per_iter, valu_per_iter) must be (4, 0|16|32|64) or (0, 32|64) (got (%d, %d))", mfma_per_iter,
+                valu_per_iter);
+  if (!sink || !aligned(sink, 4)) return fail(WOQ_ERR_INVALID_ARGUMENT, "sink must be non-NULL and 4-byte aligned");
+  if (!clocks || !aligned(clocks, 8)) return fail(WOQ_ERR_INVALID_ARGUMENT, "clocks must be non-NULL and 8-byte aligned");
+  return from_hip(woq::launch_mfma_valu(src, blocks, iters, mfma_per_iter, valu_per_iter, sink, clocks, store != 0,
+                                        static_cast<hipStream_t>(stream)),
+                  "mfma_valu launch");
+  WOQ_GUARD_END
+}
+
+size_t woq_probe_gemv_timeline_words(int64_t N) { return N >= 1 && N <= (INT64_C(1) << 31) ? woq::gemv_timeline_words(N) : 0; }
+
+woq_status woq_probe_gemv_timeline(const void* x, const void* packed, const void* scales, const void* zeros,
+                                   int64_t N, void* y, uint64_t* timeline, size_t timeline_words, void* stream) {
+  WOQ_GUARD_BEGIN
+  if (N < 1 || N > (INT64_C(1) << 31)) return fail(WOQ_ERR_INVALID_ARGUMENT, "N must be in [1, 2^31] (got %lld)", (long long)N);
+  if (!x || !aligned(x, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "x must be non-NULL and 16-byte aligned");
+  if (!packed || !aligned(packed, 16)) return fail(WOQ_ERR_INVALID_ARGUMENT, "packed must be non-NULL and 16-byte aligned");
+  if (!scales || !aligned(scales, 2)) return fail(WOQ_ERR_INVALID_ARGUMENT, "scales must be non-NULL and 2-byte aligned");
+  if (!zeros || !aligned(zeros, 2)) return fail(WOQ_ERR_INVALID_ARGUMENT, "zeros must be non-NULL and 2-byte aligned");
+  if (!y || !aligned(y, 2)) return fail(WOQ_ERR_INVALID_ARGUMENT, "y must be non-NULL and 2-byte aligned");
+  if (!timeline || !aligned(timeline, 8)) return fail(WOQ_ERR_INVALID_ARGUMENT, "timeline must be non-NULL and 8-byte aligned");
+  const size_t need = woq::gemv_timeline_words(N);
+  if (timeline_words < need)
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "timeline too small (%zu words, need %zu)", timeline_words, need);
+  return from_hip(woq::launch_gemv_timeline(x, packed, scales, zeros, N, y, timeline, static_cast<hipStream_t>(stream)),
+                  "gemv_timeline launch");
+  WOQ_GUARD_END
+}
+
 const char* woq_status_string(woq_status status) {
   switch (status) {
     case WOQ_OK:

@@ -109,4 +109,10 @@ __device__ inline float team_min(float v, int team) {
 
 __device__ inline float half_bits_to_f32(uint16_t v) { return (float)__builtin_bit_cast(_Float16, v); }
 
+// 1 / s for an activation scale: the hardware reciprocal v_rcp_f32, within
+// 1 ulp of the quotient.  Activations x * (1 / s) are rounded to a 16-bit
+// float (relative error 2^-11 or 2^-8) before use, so the reciprocal's 2^-23
+// does not show; an IEEE division costs about ten VALU instead of one.
+__device__ inline float act_recip(float s) { return __builtin_amdgcn_rcpf(s); }
+
 }  // namespace woq

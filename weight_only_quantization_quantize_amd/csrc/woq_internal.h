@@ -100,6 +100,11 @@ hipError_t launch_stream_read(const void* p, int64_t bytes, int blocks, int thre
                               int store, hipStream_t stream);
 hipError_t launch_empty(int blocks, int threads, hipStream_t stream);
 hipError_t launch_mfma_rate(const void* src, int blocks, int iters, float* sink, int store, hipStream_t stream);
+size_t gemv_timeline_words(int64_t N);
+hipError_t launch_gemv_timeline(const void* x, const void* packed, const void* scales, const void* zeros, int64_t N,
+                                void* y, uint64_t* tl, hipStream_t stream);
+hipError_t launch_mfma_valu(const void* src, int blocks, int iters, int mfma_per_iter, int valu_per_iter, float* sink,
+                            uint64_t* clocks, int store, hipStream_t stream);
 
 // Dequantize to fp32 (test aid).
 hipError_t launch_dequantize(const void* packed, const void* scales, const void* zeros, int64_t N,

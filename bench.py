@@ -247,7 +247,10 @@ def write_traffic(prof_dir, copy_mib):
 def burst_us(torch, launches, reps=3):
     """Average duration (us) of each launch when the callables in `launches`
     run back to back behind a queue prefill, HIP events on the launch stream;
-    the mean over `reps` bursts."""
+    the mean over `reps` bursts, after one untimed launch (the first launch of
+    a kernel also pays for finding its code)."""
+    launches[0]()
+    torch.cuda.synchronize()
     total = 0.0
     for _ in range(reps):
         torch.cuda.synchronize()

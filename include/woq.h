@@ -102,9 +102,16 @@ size_t woq_packed_bytes(int64_t N, int64_t K, int32_t bits);
  * Returns 0 for invalid arguments. */
 size_t woq_scales_bytes(int64_t N, int64_t K, int32_t group_size);
 
-/* Workspace bytes woq_w4a16_gemv / woq_w4a16_gemm need for this shape
- * (currently always 0: every kernel reduces in registers and LDS).  Callers
- * may pass workspace = NULL when this returns 0. */
+/* Workspace bytes woq_w4a16_gemm can use for this shape (0 for invalid
+ * arguments).  Non-zero (8 M bytes rounded up to 256, plus 2 M K bytes) for
+ * M >= 33, 4-bit codes and K % 64 == 0: there, bf16 X given a workspace at
+ * least this large (256-byte aligned, device memory the call may overwrite)
+ * runs on the fp16 mid-M (33..127 rows, where fp16 X would take it) or
+ * register-B (M >= 128) kernel through an exact per-row power-of-two rescale:
+ * the call writes each row's factors and the rescaled fp16 copy of X into the
+ * workspace; without one it takes the slower bf16 kernels.
+ * fp16 X and woq_w4a16_gemv never use a workspace, and workspace = NULL is
+ * always valid. */
 size_t woq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size);
 
 /* Quantize fp16 weights W [N, K] (row-major, output channel n, input channel
@@ -147,8 +154,15 @@ woq_status woq_w4a16_gemv(const void* x, int32_t xdtype, const float* act_scale,
  * as given and w_hat * r(s) kept as a bf16 pair
  * hi + lo (about 16 significant bits), or, for bf16 X at 33..127 rows without
  * an AWQ scale (group size a power of two >= 64), the exact 128 + u with the
- * scale applied per group in fp32.  fp32 accumulation throughout; the
- * order of the K sum inside an MFMA step is the kernel's. */
+ * scale applied per group in fp32.  bf16 X given a workspace of
+ * woq_workspace_bytes(M, N, K, bits, group_size) > 0 bytes instead runs as
+ * fp16: each row, X * r(s) with an AWQ scale, is multiplied by the power of
+ * two f_m that puts its largest magnitude in [2^14, 2^15) and converted to
+ * fp16 (exact without an AWQ scale, for every value above 2^-31 of the row's
+ * largest), the product uses w_hat rounded once to fp16, and the result is
+ * multiplied by 1 / f_m and rounded once to bf16.  fp32 accumulation
+ * throughout; the order of the K sum inside an MFMA step is the kernel's.
+ * workspace may be NULL; when given it must be 256-byte aligned. */
 woq_status woq_w4a16_gemm(const void* X, int32_t xdtype, const float* act_scale,
                           const void* packed, const void* scales, const void* zeros,
                           int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size,

@@ -55,6 +55,28 @@ def test_size_queries(lib):
     assert lib.woq_workspace_bytes(1, 8192, 8192, 4, 128) == 0
 
 
+def test_gemm_workspace_bytes(lib):
+    # bf16 rows' power-of-two factors (f_m and 1 / f_m, fp32; 8 M bytes
+    # rounded up to 256) and the rescaled fp16 copy of X (2 M K bytes), only
+    # where the rescaled route exists: M >= 33, 4-bit, K % 64 == 0
+    def need(M, K):
+        return (8 * M + 255) // 256 * 256 + 2 * M * K
+    for M, N, K in ((128, 520, 512), (300, 520, 1536), (2048, 11008, 4096), (64, 28672, 8192), (33, 520, 512)):
+        assert lib.woq_workspace_bytes(M, N, K, 4, 128) == need(M, K)
+    assert lib.woq_workspace_bytes(32, 520, 512, 4, 128) == 0
+    assert lib.woq_workspace_bytes(300, 520, 1536, 3, 128) == 0
+    assert lib.woq_workspace_bytes(300, 520, 1056, 4, 32) == 0
+    for bad in ((0, 520, 512, 4, 128), (300, 0, 512, 4, 128), (300, 520, 500, 4, 128), (300, 520, 512, 5, 128),
+                (300, 520, 512, 4, 100), (300, 520, 512, 4, 384)):
+        assert lib.woq_workspace_bytes(*bad) == 0
+
+
+def test_gemm_rejects_misaligned_workspace(lib):
+    st = lib.woq_w4a16_gemm(FAKE, 1, None, FAKE, FAKE, FAKE, 300, 520, 1536, 4, 128, 1, FAKE, FAKE + 8, 4096,
+                            None)
+    assert st == 1 and b"workspace must be 256-byte aligned" in lib.woq_last_error()
+
+
 def test_status_strings(lib):
     for code, name in [(0, "WOQ_OK"), (1, "WOQ_ERR_INVALID_ARGUMENT"), (2, "WOQ_ERR_UNSUPPORTED"),
                        (3, "WOQ_ERR_HIP"), (4, "WOQ_ERR_INTERNAL")]:

@@ -574,6 +574,85 @@ def test_gemm_large_m_tiles(xdtype, bits, asym, G, K, awq):
     gemm_case(W, X, xdtype, bits, asym, G=G, s=s, label="large-M")
 
 
+def _bf16_rows_of_every_magnitude(rng, M, K):
+    """bf16 bits [M, K]: rows scaled by 2^-100 .. 2^100, a zero row, rows
+    whose entries span 2^-40 .. 2^40 of each other, and ordinary rows."""
+    X32 = rng.standard_normal((M, K)).astype(np.float32)
+    X32[0] *= 2.0 ** 100
+    X32[1] *= 2.0 ** -100
+    X32[2] = 0.0
+    X32[3] *= np.exp2(rng.uniform(-40, 40, K)).astype(np.float32)
+    X32[4] *= 70000.0  # above fp16's largest finite value before scaling
+    X32[5, : K // 2] = 0.0
+    return synth.to_bf16_bits(X32)
+
+
+def _assert_rows_close(Yh, Y_ref, X64, q, s, label):
+    # The rows differ by up to 2^200 in magnitude.  Every row is held to the
+    # per-element bound on its own; the relative L2 bar applies to the rows
+    # normalised to unit norm (one 264-element row's bf16 output rounding
+    # alone scatters around the whole-output 1.66e-3).
+    norms = np.linalg.norm(Y_ref, axis=1)
+    live = norms > 0
+    err = O.rel_l2(Yh[live] / norms[live, None], Y_ref[live] / norms[live, None])
+    _say(f"{label}: rel_l2 of the unit-norm rows {err:.2e}")
+    assert err <= REL_L2, f"{label}: rel_l2 {err:.3e}"
+    w_hat = O.dequantize(q)
+    for m in range(Yh.shape[0]):
+        bound = output_bound(X64[m: m + 1], w_hat, q.scales, q.bits, q.group_size, s, Y_ref[m: m + 1], "bf16")
+        ok, worst, where = check_elementwise(Yh[m: m + 1], Y_ref[m: m + 1], bound)
+        assert ok, f"{label} row {m}: element {where} off by {worst:.2f}x its bound"
+
+
+@pytest.mark.parametrize("M", [96, 136])
+@pytest.mark.parametrize("awq", [False, True])
+def test_gemm_bf16_rows_of_every_magnitude(M, awq):
+    # bf16 X with a workspace runs on the fp16 mid-M (96 rows) or register-B
+    # (136 rows) kernel: each row is scaled by a power of two into fp16's
+    # range (exact), and the output scaled back.  Rows 2^200 apart, a zero
+    # row, entries spanning 2^80 inside one row and values above 65504 must
+    # all match the oracle row by row.
+    rng = np.random.default_rng(4242 + int(awq) + M)
+    N, K = 264, 512
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X = _bf16_rows_of_every_magnitude(rng, M, K)
+    s = np.exp(rng.uniform(-1.0, 1.0, K)).astype(np.float32) if awq else None
+    packed, scales, zeros = ops.quantize_pack(gpu_f16(W), 4, 128, True, gpu_f32(s))
+    assert ops._lib.call("woq_workspace_bytes", M, N, K, 4, 128) > 0
+    Y = ops.gemm(gpu_x(X, "bf16"), packed, scales, zeros, N, K, 4, 128, gpu_f32(s))
+    _, _, _, q = O.quantize_pack(W, 4, 128, True, s)
+    X64 = O.activations_f64(X, "bf16")
+    Y_ref = O.gemm(X64, O.dequantize(q), s)
+    Yh = host(Y)
+    assert np.all(Yh[2] == 0.0)
+    _assert_rows_close(Yh, Y_ref, X64, q, s, f"bf16 rescale awq={awq}")
+
+
+def test_gemm_bf16_with_and_without_workspace():
+    # The C ABI takes bf16 X without a workspace too (the bf16 LDS-staged
+    # kernel); both routes meet the oracle's bound on the same inputs.
+    rng = np.random.default_rng(5151)
+    M, N, K = 300, 520, 1536
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X = synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    packed, scales, zeros = ops.quantize_pack(gpu_f16(W), 4, 128, True)
+    Xg = gpu_x(X, "bf16")
+    need = ops._lib.call("woq_workspace_bytes", M, N, K, 4, 128)
+    assert need == (8 * M + 255) // 256 * 256 + 2 * M * K
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    _, _, _, q = O.quantize_pack(W, 4, 128, True)
+    X64 = O.activations_f64(X, "bf16")
+    Y_ref = O.gemm(X64, O.dequantize(q), None)
+    for label, wptr, wbytes in (("no workspace", None, 0), ("workspace", ws.data_ptr(), need),
+                                ("short workspace", ws.data_ptr(), need - 256)):
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+        st = ops._lib.call("woq_w4a16_gemm", Xg.data_ptr(), 1, None, packed.data_ptr(), scales.data_ptr(),
+                           zeros.data_ptr(), M, N, K, 4, 128, 1, Y.data_ptr(), wptr, wbytes,
+                           torch.cuda.current_stream().cuda_stream)
+        ops._lib.check(st, f"woq_w4a16_gemm ({label})")
+        assert_output_close(host(Y), Y_ref, X64, q, None, "bf16", f"bf16 prefill, {label}")
+
+
 @pytest.mark.parametrize("G,asym", [(256, True), (128, True), (64, False), (64, True)])
 def test_gemm_large_m_scale_staging(G, asym):
     # fp16 register-B kernel with K / G a multiple of 8 (8, 16, 32 groups per

@@ -493,6 +493,134 @@ bool gemm_uses_mid(int64_t M, int64_t N, int64_t K, int bits, int xdtype, bool s
          (M > 64 || N >= kMidMinN || !skinny_ok);
 }
 
+namespace {
+
+// bf16 X on the fp16 MFMA kernels.  One workgroup per row m: f_m (rs[m])
+// is the power of two that puts the row's largest |x| (|x * act_recip(s)|
+// with an AWQ scale) in [2^14, 2^15), and X16[m] = fp16(x [* act_recip(s)]
+// * f_m); a bf16 value has 8 significant bits and fp16 11, so without an AWQ
+// scale the conversion is exact down to 2^-31 of the row's largest value,
+// and with one it is the fp16 path's single rounding of x * act_recip(s).
+// g_m = 1 / f_m (rs[M + m]) undoes the scaling in the consumer's epilogue.
+// Rows of zeros, or with an infinity, keep f_m = g_m = 1 (the infinity
+// reaches the output as it would through a bf16 product); NaNs do not enter
+// the maximum and propagate through the product.  Up to kXbUnits 16-byte
+// units per thread (K <= 16384) stay in registers between the two passes;
+// longer rows are read twice.
+constexpr int kXbThreads = 256, kXbUnits = 8;
+
+template <bool SCALE>
+__global__ __launch_bounds__(kXbThreads) void xb_rescale_kernel(const uint16_t* __restrict__ X,
+                                                               const float* __restrict__ s, int M, int K,
+                                                               uint16_t* __restrict__ X16, float* __restrict__ rs) {
+  __shared__ float wmax[kXbThreads / 64];
+  const int row = (int)blockIdx.x, tid = (int)threadIdx.x;
+  const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(X + (int64_t)row * K);
+  u32x4_t* yr = reinterpret_cast<u32x4_t*>(X16 + (int64_t)row * K);
+  const int units = K / 8;
+  const bool resident = units <= kXbThreads * kXbUnits;
+  auto value = [&](uint32_t word, int half, int u, int e) {
+    float x = BF16::to_f32((uint16_t)(word >> (16 * half)));
+    if constexpr (SCALE) x *= act_recip(s[8 * u + e]);
+    return x;
+  };
+  u32x4_t v[kXbUnits];
+  float mx = 0.0f;
+  for (int u0 = 0; u0 < units; u0 += kXbThreads * kXbUnits) {
+#pragma unroll
+    for (int i = 0; i < kXbUnits; ++i) {
+      const int u = u0 + tid + kXbThreads * i;
+      if (u < units) v[i] = xr[u];
+    }
+#pragma unroll
+    for (int i = 0; i < kXbUnits; ++i) {
+      const int u = u0 + tid + kXbThreads * i;
+      if (u < units) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(value(v[i][e / 2], e & 1, u, e)));
+      }
+    }
+  }
+  mx = team_max(mx, 64);
+  if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kXbThreads / 64; ++w) mx = fmaxf(mx, wmax[w]);
+  float f = 1.0f;
+  if (mx > 0.0f && mx <= 3.40282347e38f) {
+    int ef = 14 - ilogbf(mx);
+    ef = ef < 127 ? ef : 127;
+    f = ldexpf(1.0f, ef);
+    if (tid == 0) {
+      rs[row] = f;
+      rs[M + row] = ldexpf(1.0f, -ef);
+    }
+  } else if (tid == 0) {
+    rs[row] = 1.0f;
+    rs[M + row] = 1.0f;
+  }
+  for (int u0 = 0; u0 < units; u0 += kXbThreads * kXbUnits) {
+#pragma unroll
+    for (int i = 0; i < kXbUnits; ++i) {
+      const int u = u0 + tid + kXbThreads * i;
+      if (u < units) {
+        const u32x4_t w = resident ? v[i] : xr[u];
+        u32x4_t o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = (uint32_t)F16::from_f32(value(w[e], 0, u, 2 * e) * f) |
+                 ((uint32_t)F16::from_f32(value(w[e], 1, u, 2 * e + 1) * f) << 16);
+        yr[u] = o;
+      }
+    }
+  }
+}
+
+// Shapes whose bf16 X can run on the fp16 mid-M or register-B kernel.
+bool xb_rescale_ok(int64_t M, int64_t K, int bits) { return M >= kMidMinM && bits == 4 && K % 64 == 0; }
+
+}  // namespace
+
+// Workspace of the bf16 route: f_m and g_m (8 M bytes, rounded up to 256),
+// then the rescaled fp16 copy of X (2 M K bytes).
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits, int group_size) {
+  (void)N;
+  (void)group_size;
+  if (!xb_rescale_ok(M, K, bits)) return 0;
+  return (size_t)((8 * M + 255) / 256 * 256) + (size_t)(2 * M * K);
+}
+
+hipError_t launch_gemm_ws(const void* X, int xdtype, const float* act_scale, const void* packed, const void* scales,
+                          const void* zeros, int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                          bool asymmetric, void* Y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const size_t need = gemm_workspace_bytes(M, N, K, bits, group_size);
+  if (xdtype == 1 && need > 0 && workspace && workspace_bytes >= need) {
+    // the fp16 kernels' own routing: register-B from 128 rows, mid-M below
+    // where it would take fp16 X (the bf16 small-batch kernel keeps the rest)
+    const bool regb = M >= kLdsGemmMinM;
+    const bool mid = !regb && gemm_uses_mid(M, N, K, bits, 0,
+                                            gemm_skinny_supported(M, N, K, xdtype, act_scale != nullptr, bits,
+                                                                  group_size, scales, zeros));
+    if (regb || mid) {
+      float* rs = static_cast<float*>(workspace);
+      uint16_t* X16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + (8 * M + 255) / 256 * 256);
+      if (act_scale)
+        hipLaunchKernelGGL(xb_rescale_kernel<true>, dim3((unsigned)M), dim3(kXbThreads), 0, stream,
+                           static_cast<const uint16_t*>(X), act_scale, (int)M, (int)K, X16, rs);
+      else
+        hipLaunchKernelGGL(xb_rescale_kernel<false>, dim3((unsigned)M), dim3(kXbThreads), 0, stream,
+                           static_cast<const uint16_t*>(X), act_scale, (int)M, (int)K, X16, rs);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      // the activation scale is in X16 already
+      return regb ? launch_gemm_regb_bf16(X16, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, rs, stream)
+                  : launch_gemm_mid_rescaled_bf16(X16, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, rs,
+                                                  stream);
+    }
+  }
+  return launch_gemm(X, xdtype, act_scale, packed, scales, zeros, M, N, K, bits, group_size, asymmetric, Y, stream);
+}
+
 hipError_t launch_gemm(const void* X, int xdtype, const float* act_scale, const void* packed, const void* scales,
                        const void* zeros, int64_t M, int64_t N, int64_t K, int bits, int group_size, bool asymmetric,
                        void* Y, hipStream_t stream) {

@@ -29,6 +29,11 @@
 //     groups), from 16-byte loads when both arrays are 16-byte aligned and
 //     K / G % 8 == 0.
 //
+// bf16 X (XB) runs on the same fp16 MFMAs through the exact per-row
+// power-of-two rescale of the register-B kernel: X is the pre-pass's fp16
+// copy of fp16(x * f_m), and the output is multiplied by g_m = 1 / f_m
+// before its one rounding to bf16 (g_m from the caller's workspace).
+//
 // MFMA operand slots (32x32x16): lane l supplies A[m = l%32][8(l/32)+j] and
 // B[8(l/32)+j][n = l%32] and holds C[m = 8(v/4) + 4(l/32) + v%4][n = l%32]
 // in accumulator v = 0..15.
@@ -69,14 +74,14 @@ __device__ inline uint32_t dequant_pair(uint32_t magic_codes2, uint32_t zmagic2,
 // kRing: K steps of loads in flight.  4 for a single row of tiles (M <= 64:
 // one workgroup per compute unit at most, so the ring's registers cost no
 // occupancy), 3 otherwise (two workgroups per compute unit).
-template <bool ASYM, bool SCALE, int SZ, int kRing>
+template <bool ASYM, bool SCALE, int SZ, int kRing, bool XB>
 __global__ __launch_bounds__(kThreads, kRing == 3 ? 2 : 1) void gemm_mid_kernel(const uint16_t* __restrict__ X,
                                                                const float* __restrict__ s,
                                                                const uint8_t* __restrict__ packed,
                                                                const uint16_t* __restrict__ scales,
                                                                const uint16_t* __restrict__ zeros, int M, int N, int K,
                                                                int G, uint16_t* __restrict__ Y, int tiles_m,
-                                                               int tiles_n) {
+                                                               int tiles_n, const float* __restrict__ rs) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kStage];  // [K half][stage]
   constexpr bool SZL = SZ > 0;
   __shared__ uint32_t szs[SZL ? kSZWords : 1];
@@ -115,6 +120,7 @@ __global__ __launch_bounds__(kThreads, kRing == 3 ? 2 : 1) void gemm_mid_kernel(
   }
   const uint32_t a_dst = (uint32_t)(a_r0 * kLD + 8 * a_seg);
   uint16_t* const my_stages = lds + 2 * kh * kStage;
+
 
   // B: column n0 + 32 cg + l%32 (columns past N read column N - 1, never
   // stored); this lane's chunk of the block starting at k is codes
@@ -309,39 +315,59 @@ __global__ __launch_bounds__(kThreads, kRing == 3 ? 2 : 1) void gemm_mid_kernel(
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int dm = 32 * i + 8 * (v >> 2) + (v & 3);
-      if (row_base + dm < M) yb[(int64_t)dm * N] = F16::from_f32(acc[i][v]);
+      if constexpr (XB) {
+        // undo the row scaling (g_m = 1 / f_m: exact), then one rounding to bf16
+        const int r = row_base + dm;
+        if (r < M) yb[(int64_t)dm * N] = BF16::from_f32(acc[i][v] * rs[M + r]);
+      } else {
+        if (row_base + dm < M) yb[(int64_t)dm * N] = F16::from_f32(acc[i][v]);
+      }
     }
 }
 
-template <bool ASYM, bool SCALE, int SZ>
+template <bool ASYM, bool SCALE, int SZ, bool XB>
 hipError_t launch_sz(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
-                     int64_t M, int64_t N, int64_t K, int G, void* Y, hipStream_t stream) {
+                     int64_t M, int64_t N, int64_t K, int G, void* Y, const float* rs, hipStream_t stream) {
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
   const int T = tiles_m * tiles_n;
   const unsigned blocks = 8u * (unsigned)((T + 7) / 8);  // blockIdx.x % 8 is the XCD
   if (tiles_m == 1)
-    hipLaunchKernelGGL((gemm_mid_kernel<ASYM, SCALE, SZ, 4>), dim3(blocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((gemm_mid_kernel<ASYM, SCALE, SZ, 4, XB>), dim3(blocks), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
                        static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N,
-                       (int)K, G, static_cast<uint16_t*>(Y), tiles_m, tiles_n);
+                       (int)K, G, static_cast<uint16_t*>(Y), tiles_m, tiles_n, rs);
   else
-    hipLaunchKernelGGL((gemm_mid_kernel<ASYM, SCALE, SZ, 3>), dim3(blocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((gemm_mid_kernel<ASYM, SCALE, SZ, 3, XB>), dim3(blocks), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
                        static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N,
-                       (int)K, G, static_cast<uint16_t*>(Y), tiles_m, tiles_n);
+                       (int)K, G, static_cast<uint16_t*>(Y), tiles_m, tiles_n, rs);
   return hipGetLastError();
 }
 
-template <bool ASYM, bool SCALE>
+template <bool ASYM, bool SCALE, bool XB>
 hipError_t launch_one(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
-                      int64_t M, int64_t N, int64_t K, int G, void* Y, hipStream_t stream) {
+                      int64_t M, int64_t N, int64_t K, int G, void* Y, const float* rs, hipStream_t stream) {
   const int64_t gpr = K / G;
-  if (gpr > kSZMaxGroups) return launch_sz<ASYM, SCALE, 0>(X, s, packed, scales, zeros, M, N, K, G, Y, stream);
+  if (gpr > kSZMaxGroups)
+    return launch_sz<ASYM, SCALE, 0, XB>(X, s, packed, scales, zeros, M, N, K, G, Y, rs, stream);
   const bool aligned16 = (reinterpret_cast<uintptr_t>(scales) % 16 == 0) &&
                          (!ASYM || reinterpret_cast<uintptr_t>(zeros) % 16 == 0);
   if (gpr % 8 == 0 && aligned16)
-    return launch_sz<ASYM, SCALE, 2>(X, s, packed, scales, zeros, M, N, K, G, Y, stream);
-  return launch_sz<ASYM, SCALE, 1>(X, s, packed, scales, zeros, M, N, K, G, Y, stream);
+    return launch_sz<ASYM, SCALE, 2, XB>(X, s, packed, scales, zeros, M, N, K, G, Y, rs, stream);
+  return launch_sz<ASYM, SCALE, 1, XB>(X, s, packed, scales, zeros, M, N, K, G, Y, rs, stream);
+}
+
+template <bool XB>
+hipError_t launch_xb(const void* X, const float* act_scale, const void* packed, const void* scales, const void* zeros,
+                     int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric, void* Y, const float* rs,
+                     hipStream_t stream) {
+  if (asymmetric)
+    return act_scale
+               ? launch_one<true, true, XB>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, rs, stream)
+               : launch_one<true, false, XB>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, rs, stream);
+  return act_scale
+             ? launch_one<false, true, XB>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, rs, stream)
+             : launch_one<false, false, XB>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, rs, stream);
 }
 
 }  // namespace
@@ -349,11 +375,16 @@ hipError_t launch_one(const void* X, const float* s, const void* packed, const v
 hipError_t launch_gemm_mid(const void* X, const float* act_scale, const void* packed, const void* scales,
                            const void* zeros, int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric,
                            void* Y, hipStream_t stream) {
-  if (asymmetric)
-    return act_scale ? launch_one<true, true>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream)
-                     : launch_one<true, false>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream);
-  return act_scale ? launch_one<false, true>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream)
-                   : launch_one<false, false>(X, act_scale, packed, scales, zeros, M, N, K, group_size, Y, stream);
+  return launch_xb<false>(X, act_scale, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, nullptr, stream);
+}
+
+hipError_t launch_gemm_mid_rescaled_bf16(const void* X16, const void* packed, const void* scales, const void* zeros,
+                                         int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric, void* Y,
+                                         const float* row_scales, hipStream_t stream) {
+  return asymmetric ? launch_one<true, false, true>(X16, nullptr, packed, scales, zeros, M, N, K, group_size, Y,
+                                                    row_scales, stream)
+                    : launch_one<false, false, true>(X16, nullptr, packed, scales, zeros, M, N, K, group_size, Y,
+                                                     row_scales, stream);
 }
 
 }  // namespace woq

@@ -35,6 +35,14 @@
 // that each of the 8 XCDs works on a contiguous range of the tile grid with
 // the N tile index fastest.
 //
+// bf16 X (XB) runs on the same fp16 MFMAs: a pre-pass (xb_rescale_kernel)
+// writes row m of X, times the power of two f_m that puts its largest |x|
+// in [2^14, 2^15), as fp16 into the caller's workspace; a bf16 value has 8
+// significant bits and fp16 has 11, so the conversion is exact down to 2^-31
+// of the row's largest value (fp16 subnormals below that lose bits).  This
+// kernel then runs on that fp16 copy exactly as for fp16 X, and its epilogue
+// multiplies row m by g_m = 1 / f_m (a power of two) and writes bf16.
+//
 // MFMA operand slots (32x32x16): lane l supplies A[m = l%32][8(l/32)+j] and
 // B[8(l/32)+j][n = l%32] (j = 0..7, here K offsets 32(l/32) + 8s + j) and
 // holds C[m = 8(v/4) + 4(l/32) + v%4][n = l%32] in accumulator v = 0..15.
@@ -79,11 +87,13 @@ __device__ inline uint32_t dequant_pair(uint32_t magic_codes2, uint32_t zmagic2,
 //   1: staged in LDS once per tile with 2-byte loads;
 //   2: staged in LDS once per tile from 16-byte loads, every load issued
 //      before the first is waited for (arrays 16-byte aligned, K / G % 8 == 0).
-template <bool ASYM, bool SCALE, int SZ>
+// XB: X is the rescaled fp16 copy of bf16 X and Y is bf16; rs holds f_m
+// (M floats) then g_m (M floats).
+template <bool ASYM, bool SCALE, int SZ, bool XB>
 __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ s, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int M, int N, int K, int G,
-    uint16_t* __restrict__ Y, int tiles_m, int tiles_n, RegbBatch bt) {
+    uint16_t* __restrict__ Y, int tiles_m, int tiles_n, RegbBatch bt, const float* __restrict__ rs) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
   // Batch entry blockIdx.y (one entry unless batched): its own scale vector,
   // packed set and output over the same X.
@@ -121,6 +131,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
     a_src[i] = X + (int64_t)(r < M ? r : M - 1) * K + 8 * a_seg;
   }
   const uint32_t a_dst = (uint32_t)(a_r0 * kLD + 8 * a_seg);
+  // XB: g_m of the tile's rows, in LDS (registers are at the limit of two
+  // workgroups per compute unit); read only after the loop's barriers.
+  __shared__ float g_tile[XB ? kBM : 1];
+  if constexpr (XB) {
+    if (tid < kBM) {
+      const int r = m0 + tid;
+      g_tile[tid] = rs[M + (r < M ? r : M - 1)];
+    }
+  }
 
   // B: subtile j of this wave is column n0 + 64 wave + 32 j + l%32 (columns
   // past N read column N - 1, never stored); this lane's chunk of a block
@@ -316,6 +335,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
     __syncthreads();
   }
 
+  // XB: the accumulators hold the product of the rescaled rows; row m's
+  // output is bf16(acc) * g_m with g_m = 1 / f_m a power of two, so the
+  // multiply after the rounding is exact (bf16 has fp32's exponent range)
+  // and bf16(acc) * g_m = bf16(acc * g_m).  Applying it to the 16-bit
+  // values keeps the 128 accumulators free of a second live copy.
+  auto unscale = [&](uint16_t b, int row) -> uint16_t {
+    return BF16::from_f32(BF16::to_f32(b) * g_tile[row]);
+  };
+  auto out16 = [](float v) -> uint16_t { return XB ? BF16::from_f32(v) : F16::from_f32(v); };
+
   // Epilogue, full tiles with N % 8 == 0 and the scales staged in LDS (both
   // LDS arrays are free after the loop's last barrier): each wave writes its
   // 128 x 64 fp16 block into a region of its own (pitch 72 halves) and stores
@@ -333,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
         for (int v = 0; v < 16; ++v)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            region[(32 * i + 8 * (v >> 2) + 4 * fh + (v & 3)) * kOP + 32 * j + fr] = F16::from_f32(acc[i][j][v]);
+            region[(32 * i + 8 * (v >> 2) + 4 * fh + (v & 3)) * kOP + 32 * j + fr] = out16(acc[i][j][v]);
       // the lanes of this wave read what other lanes wrote: keep the reads
       // after the writes (a wavefront-scope fence; LDS order does the rest)
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -342,7 +371,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
 #pragma unroll
       for (int it = 0; it < kBM / 8; ++it) {
         const int row = 8 * it + (lane >> 3);
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(region + row * kOP + 8 * ch);
+        u32x4_t v = *reinterpret_cast<const u32x4_t*>(region + row * kOP + 8 * ch);
+        if constexpr (XB) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = (uint32_t)unscale((uint16_t)(v[e] & 0xFFFFu), row) | ((uint32_t)unscale((uint16_t)(v[e] >> 16), row) << 16);
+        }
         *reinterpret_cast<u32x4_t*>(ybase + (int64_t)row * N) = v;
       }
       return;
@@ -355,16 +389,24 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
   uint16_t* __restrict__ yb = Y + (int64_t)row_base * N + col_base;
   if (m0 + kBM <= M && n0 + kBN <= N) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (XB) asm volatile("" ::: "memory");  // keep each group's g_tile reads in place
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        uint16_t* __restrict__ yr = yb + (int64_t)(32 * i + 8 * (v >> 2) + (v & 3)) * N;
+        const int dm = 32 * i + 8 * (v >> 2) + (v & 3);
+        uint16_t* __restrict__ yr = yb + (int64_t)dm * N;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) yr[32 * j] = F16::from_f32(acc[i][j][v]);
+        for (int j = 0; j < 2; ++j) {
+          uint16_t o = out16(acc[i][j][v]);
+          if constexpr (XB) o = unscale(o, 4 * fh + dm);
+          yr[32 * j] = o;
+        }
       }
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (XB) asm volatile("" ::: "memory");  // keep each group's g_tile reads in place
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int dm = 32 * i + 8 * (v >> 2) + (v & 3);
@@ -372,46 +414,56 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
         uint16_t* __restrict__ yr = yb + (int64_t)dm * N;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          if (col_base + 32 * j < N) yr[32 * j] = F16::from_f32(acc[i][j][v]);
+          if (col_base + 32 * j < N) {
+            uint16_t o = out16(acc[i][j][v]);
+            if constexpr (XB) o = unscale(o, 4 * fh + dm);
+            yr[32 * j] = o;
+          }
       }
+    }
   }
 }
 
-template <bool ASYM, bool SCALE, int SZ>
+template <bool ASYM, bool SCALE, int SZ, bool XB>
 hipError_t launch_sz(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
-                     int64_t M, int64_t N, int64_t K, int G, void* Y, int batch, RegbBatch bt, hipStream_t stream) {
+                     int64_t M, int64_t N, int64_t K, int G, void* Y, int batch, RegbBatch bt, const float* rs,
+                     hipStream_t stream) {
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
   const int T = tiles_m * tiles_n;
   // a multiple of 8, so that blockIdx.x % 8 is the XCD also in a batched grid
   const unsigned blocks = 8u * (unsigned)((T + 7) / 8);
-  hipLaunchKernelGGL((gemm_regb_kernel<ASYM, SCALE, SZ>), dim3(blocks, (unsigned)batch), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((gemm_regb_kernel<ASYM, SCALE, SZ, XB>), dim3(blocks, (unsigned)batch), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(X), s, static_cast<const uint8_t*>(packed),
                      static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), (int)M, (int)N, (int)K,
-                     G, static_cast<uint16_t*>(Y), tiles_m, tiles_n, bt);
+                     G, static_cast<uint16_t*>(Y), tiles_m, tiles_n, bt, rs);
   return hipGetLastError();
 }
 
-template <bool ASYM, bool SCALE>
+template <bool ASYM, bool SCALE, bool XB>
 hipError_t launch_one(const void* X, const float* s, const void* packed, const void* scales, const void* zeros,
-                      int64_t M, int64_t N, int64_t K, int G, void* Y, int batch, RegbBatch bt, hipStream_t stream) {
+                      int64_t M, int64_t N, int64_t K, int G, void* Y, int batch, RegbBatch bt, const float* rs,
+                      hipStream_t stream) {
   const int64_t gpr = K / G;
   if (gpr > kSZMaxGroups)
-    return launch_sz<ASYM, SCALE, 0>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream);
+    return launch_sz<ASYM, SCALE, 0, XB>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, rs, stream);
   const bool aligned16 = (reinterpret_cast<uintptr_t>(scales) % 16 == 0) &&
                          (!ASYM || reinterpret_cast<uintptr_t>(zeros) % 16 == 0) && bt.sz_stride % 8 == 0;
   if (gpr % 8 == 0 && aligned16)
-    return launch_sz<ASYM, SCALE, 2>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream);
-  return launch_sz<ASYM, SCALE, 1>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream);
+    return launch_sz<ASYM, SCALE, 2, XB>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, rs, stream);
+  return launch_sz<ASYM, SCALE, 1, XB>(X, s, packed, scales, zeros, M, N, K, G, Y, batch, bt, rs, stream);
 }
 
+template <bool XB = false>
 hipError_t launch_any(const void* X, const float* act_scale, const void* packed, const void* scales,
                       const void* zeros, int64_t M, int64_t N, int64_t K, int G, bool asymmetric, void* Y, int batch,
-                      RegbBatch bt, hipStream_t stream) {
+                      RegbBatch bt, const float* rs, hipStream_t stream) {
   if (asymmetric)
-    return act_scale ? launch_one<true, true>(X, act_scale, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream)
-                     : launch_one<true, false>(X, act_scale, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream);
-  return act_scale ? launch_one<false, true>(X, act_scale, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream)
-                   : launch_one<false, false>(X, act_scale, packed, scales, zeros, M, N, K, G, Y, batch, bt, stream);
+    return act_scale
+               ? launch_one<true, true, XB>(X, act_scale, packed, scales, zeros, M, N, K, G, Y, batch, bt, rs, stream)
+               : launch_one<true, false, XB>(X, act_scale, packed, scales, zeros, M, N, K, G, Y, batch, bt, rs, stream);
+  return act_scale
+             ? launch_one<false, true, XB>(X, act_scale, packed, scales, zeros, M, N, K, G, Y, batch, bt, rs, stream)
+             : launch_one<false, false, XB>(X, act_scale, packed, scales, zeros, M, N, K, G, Y, batch, bt, rs, stream);
 }
 
 }  // namespace
@@ -419,16 +471,26 @@ hipError_t launch_any(const void* X, const float* act_scale, const void* packed,
 hipError_t launch_gemm_regb(const void* X, const float* act_scale, const void* packed, const void* scales,
                             const void* zeros, int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric,
                             void* Y, hipStream_t stream) {
-  return launch_any(X, act_scale, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, 1, RegbBatch{0, 0, 0, 0},
-                    stream);
+  return launch_any<false>(X, act_scale, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, 1,
+                           RegbBatch{0, 0, 0, 0}, nullptr, stream);
+}
+
+hipError_t launch_gemm_regb_bf16(const void* X16, const void* packed, const void* scales, const void* zeros,
+                                 int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric, void* Y,
+                                 const float* row_scales, hipStream_t stream) {
+  const RegbBatch one{0, 0, 0, 0};
+  return asymmetric ? launch_one<true, false, true>(X16, nullptr, packed, scales, zeros, M, N, K, group_size, Y, 1,
+                                                    one, row_scales, stream)
+                    : launch_one<false, false, true>(X16, nullptr, packed, scales, zeros, M, N, K, group_size, Y, 1,
+                                                     one, row_scales, stream);
 }
 
 hipError_t launch_gemm_regb_batched(const void* X, const float* act_scale, int64_t s_stride, const void* packed,
                                     int64_t packed_stride, const void* scales, const void* zeros, int64_t sz_stride,
                                     int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric, void* Y,
                                     int64_t y_stride, int batch, hipStream_t stream) {
-  return launch_any(X, act_scale, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, batch,
-                    RegbBatch{s_stride, packed_stride, sz_stride, y_stride}, stream);
+  return launch_any<false>(X, act_scale, packed, scales, zeros, M, N, K, group_size, asymmetric, Y, batch,
+                           RegbBatch{s_stride, packed_stride, sz_stride, y_stride}, nullptr, stream);
 }
 
 }  // namespace woq

@@ -143,12 +143,10 @@ size_t woq_scales_bytes(int64_t N, int64_t K, int32_t group_size) {
 }
 
 size_t woq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t bits, int32_t group_size) {
-  (void)M;
-  (void)N;
-  (void)K;
-  (void)bits;
-  (void)group_size;
-  return 0;
+  if (M < 1 || M > INT32_MAX / 2 || N < 1 || N > INT32_MAX || K < 32 || K % 32 != 0 || K > INT32_MAX / 2 ||
+      (bits != 3 && bits != 4) || group_size < 32 || group_size % 32 != 0 || K % group_size != 0)
+    return 0;
+  return woq::gemm_workspace_bytes(M, N, K, bits, group_size);
 }
 
 woq_status woq_quantize_pack(const void* W, const float* act_scale, int64_t N, int64_t K, int32_t bits,
@@ -197,10 +195,10 @@ woq_status woq_w4a16_gemm(const void* X, int32_t xdtype, const float* act_scale,
                           int32_t group_size, int32_t asymmetric, void* Y, void* workspace, size_t workspace_bytes,
                           void* stream) {
   WOQ_GUARD_BEGIN
-  (void)workspace;
-  (void)workspace_bytes;
   WOQ_TRY(check_qparams(N, K, bits, group_size));
   if (M < 1) return fail(WOQ_ERR_INVALID_ARGUMENT, "M must be >= 1 (got %lld)", (long long)M);
+  if (workspace && !aligned(workspace, 256))
+    return fail(WOQ_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned when given");
   if (M > INT32_MAX / 2) return fail(WOQ_ERR_UNSUPPORTED, "M too large for this library (%lld)", (long long)M);
   if (xdtype != WOQ_F16 && xdtype != WOQ_BF16)
     return fail(WOQ_ERR_INVALID_ARGUMENT, "xdtype must be WOQ_F16 or WOQ_BF16 (got %d)", xdtype);
@@ -214,8 +212,8 @@ woq_status woq_w4a16_gemm(const void* X, int32_t xdtype, const float* act_scale,
     return from_hip(woq::launch_gemv(X, xdtype, act_scale, packed, scales, zeros, N, K, bits, group_size,
                                      asymmetric != 0, Y, st),
                     "gemm (M=1) launch");
-  return from_hip(woq::launch_gemm(X, xdtype, act_scale, packed, scales, zeros, M, N, K, bits, group_size,
-                                   asymmetric != 0, Y, st),
+  return from_hip(woq::launch_gemm_ws(X, xdtype, act_scale, packed, scales, zeros, M, N, K, bits, group_size,
+                                      asymmetric != 0, Y, workspace, workspace_bytes, st),
                   "gemm launch");
   WOQ_GUARD_END
 }

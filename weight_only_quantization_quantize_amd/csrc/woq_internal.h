@@ -24,6 +24,16 @@ hipError_t launch_gemm(const void* X, int xdtype, const float* act_scale, const 
                        const void* scales, const void* zeros, int64_t M, int64_t N, int64_t K, int bits,
                        int group_size, bool asymmetric, void* Y, hipStream_t stream);
 
+// launch_gemm with the caller's workspace: bf16 X at shapes where
+// gemm_workspace_bytes is non-zero runs on the fp16 register-B kernel
+// through an exact per-row power-of-two rescale (row scales in the
+// workspace) when the workspace is given and large enough.
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits, int group_size);
+hipError_t launch_gemm_ws(const void* X, int xdtype, const float* act_scale, const void* packed,
+                          const void* scales, const void* zeros, int64_t M, int64_t N, int64_t K, int bits,
+                          int group_size, bool asymmetric, void* Y, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
 // Whether launch_gemm takes the register-B kernel for this shape.
 bool gemm_uses_regb(int64_t M, int64_t N, int64_t K, int bits, int xdtype);
 
@@ -38,6 +48,12 @@ hipError_t launch_gemm_lds(const void* X, int xdtype, const float* act_scale, co
 hipError_t launch_gemm_regb(const void* X, const float* act_scale, const void* packed, const void* scales,
                             const void* zeros, int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric,
                             void* Y, hipStream_t stream);
+// The same kernel for bf16 Y: X16 is the fp16 copy of bf16 X with row m
+// multiplied by f_m (and by the activation scale's reciprocal, if any);
+// row_scales holds f_m (M floats) then 1 / f_m, which the epilogue applies.
+hipError_t launch_gemm_regb_bf16(const void* X16, const void* packed, const void* scales, const void* zeros,
+                                 int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric, void* Y,
+                                 const float* row_scales, hipStream_t stream);
 // The same for `batch` products over one X: entry b uses act_scale + b
 // s_stride, packed + b packed_stride (bytes), scales / zeros + b sz_stride
 // and writes Y + b y_stride (elements); one launch fills the chip where one
@@ -47,6 +63,11 @@ hipError_t launch_gemm_regb(const void* X, const float* act_scale, const void* p
 hipError_t launch_gemm_mid(const void* X, const float* act_scale, const void* packed, const void* scales,
                            const void* zeros, int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric,
                            void* Y, hipStream_t stream);
+// The same kernel for bf16 Y on the rescaled fp16 copy X16 (as for
+// launch_gemm_regb_bf16).
+hipError_t launch_gemm_mid_rescaled_bf16(const void* X16, const void* packed, const void* scales, const void* zeros,
+                                         int64_t M, int64_t N, int64_t K, int group_size, bool asymmetric, void* Y,
+                                         const float* row_scales, hipStream_t stream);
 bool gemm_uses_mid(int64_t M, int64_t N, int64_t K, int bits, int xdtype, bool skinny_ok);
 // Mid-M GEMM for bf16 X and 4-bit codes (K % 64 == 0, G a power of two >= 64,
 // no AWQ scale): the same tiles with the weights kept exact as 128 + u and the

@@ -19,6 +19,21 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+# One GEMM workspace per (device, stream), grown on demand and kept for the
+# life of the process: calls on one stream run in stream order, so they can
+# share it, and allocating it per call cost more host time than a short GEMM.
+_WORKSPACES: dict = {}
+
+
+def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    key = (device.index, stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -156,9 +171,16 @@ def gemm(
         _check_out(out, (M, N), X.dtype, "out")
     Y = out if out is not None else torch.empty((M, N), dtype=X.dtype, device=X.device)
     _require_gpu(X, act_scale, packed, scales, zeros, Y)
+    # bf16 X can run on the fp16 kernels through a per-row rescale: the row
+    # factors and the rescaled fp16 copy of X live in a workspace
+    ws, ws_bytes = None, 0
+    if X.dtype == torch.bfloat16:
+        ws_bytes = int(_lib.call("woq_workspace_bytes", M, N, K, bits, group_size))
+        if ws_bytes:
+            ws = _workspace(X.device, _stream(X), ws_bytes)
     st = _lib.call("woq_w4a16_gemm", X.data_ptr(), _DTYPE[X.dtype], _ptr(act_scale), packed.data_ptr(),
                    scales.data_ptr(), _ptr(zeros), M, N, K, bits, group_size, int(zeros is not None), Y.data_ptr(),
-                   None, 0, _stream(X))
+                   _ptr(ws), ws_bytes, _stream(X))
     _lib.check(st, "woq_w4a16_gemm")
     return Y
 

@@ -489,7 +489,8 @@ constexpr int64_t kMidMinM = 33;
 constexpr int64_t kMidMinN = 16384;
 
 bool gemm_uses_mid(int64_t M, int64_t N, int64_t K, int bits, int xdtype, bool skinny_ok) {
-  return M >= kMidMinM && M < kLdsGemmMinM && xdtype == 0 && bits == 4 && K % 64 == 0 &&
+  // K < 2^16: the kernel's group index by multiplication needs K * G < 2^32
+  return M >= kMidMinM && M < kLdsGemmMinM && xdtype == 0 && bits == 4 && K % 64 == 0 && K < 65536 &&
          (M > 64 || N >= kMidMinN || !skinny_ok);
 }
 

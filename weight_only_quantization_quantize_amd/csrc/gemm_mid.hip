@@ -73,9 +73,15 @@ __device__ inline uint32_t dequant_pair(uint32_t magic_codes2, uint32_t zmagic2,
 // in LDS with 2-byte loads; 2 = staged from 16-byte loads.
 // kRing: K steps of loads in flight.  4 for a single row of tiles (M <= 64:
 // one workgroup per compute unit at most, so the ring's registers cost no
-// occupancy), 3 otherwise (two workgroups per compute unit).
+// occupancy), 3 otherwise (two workgroups per compute unit: 4 waves per SIMD,
+// at most 128 VGPRs each; the launch bound's second value is waves per SIMD).
+// With one workgroup per compute unit the loads go through buffer resources
+// (a 32-bit offset per lane, the block offset in a scalar register: no
+// address arithmetic per load) and the group index is one multiply per step
+// instead of a division (c4 M = 64: 54.1 -> 51.5 us, same bits); at 128 VGPRs
+// the same code spills, so the two-workgroup instance keeps pointer loads.
 template <bool ASYM, bool SCALE, int SZ, int kRing, bool XB>
-__global__ __launch_bounds__(kThreads, kRing == 3 ? 2 : 1) void gemm_mid_kernel(const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(kThreads, kRing == 3 ? 4 : 2) void gemm_mid_kernel(const uint16_t* __restrict__ X,
                                                                const float* __restrict__ s,
                                                                const uint8_t* __restrict__ packed,
                                                                const uint16_t* __restrict__ scales,
@@ -84,6 +90,7 @@ __global__ __launch_bounds__(kThreads, kRing == 3 ? 2 : 1) void gemm_mid_kernel(
                                                                int tiles_n, const float* __restrict__ rs) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kStage];  // [K half][stage]
   constexpr bool SZL = SZ > 0;
+  constexpr bool kLean = kRing == 4;
   __shared__ uint32_t szs[SZL ? kSZWords : 1];
 
   // Tiles in XCD-contiguous ranges, N tile fastest.
@@ -113,11 +120,15 @@ __global__ __launch_bounds__(kThreads, kRing == 3 ? 2 : 1) void gemm_mid_kernel(
   // Rows past M read row M - 1; their outputs are never stored.
   const int a_seg = htid % kASegs, a_r0 = htid / kASegs;
   const uint16_t* a_src[kAUnits];
+  uint32_t a_off[kAUnits];  // kLean: byte offsets from X (2 M K < 2^31)
 #pragma unroll
   for (int i = 0; i < kAUnits; ++i) {
     const int r = m0 + a_r0 + kARowStep * i;
     a_src[i] = X + (int64_t)(r < M ? r : M - 1) * K + 8 * a_seg;
+    a_off[i] = 2u * (uint32_t)((r < M ? r : M - 1) * K + 8 * a_seg);
   }
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), 0, 2 * M * K, kBufferWord3);
   const uint32_t a_dst = (uint32_t)(a_r0 * kLD + 8 * a_seg);
   uint16_t* const my_stages = lds + 2 * kh * kStage;
 
@@ -129,6 +140,20 @@ __global__ __launch_bounds__(kThreads, kRing == 3 ? 2 : 1) void gemm_mid_kernel(
   bc = bc < N ? bc : N - 1;
   const uint8_t* b_src = packed + (int64_t)bc * (K / 2) + 16 * fh;
   const int64_t g_row = (int64_t)bc * gpr;
+  const int64_t b_bytes = ((int64_t)N - n0) * (K / 2);  // kLean: the tile's columns onward
+  const __amdgpu_buffer_rsrc_t b_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(packed + (int64_t)n0 * (K / 2)), 0,
+                                        (int)(b_bytes < 0x7FFFFFFF ? b_bytes : 0x7FFFFFFF), kBufferWord3);
+  const uint32_t b_off = (uint32_t)((bc - n0) * (K / 2) + 16 * fh);
+  // Group of this lane's chunk of the block at kb, (kb + 32 h) / G: kLean
+  // multiplies by ceil(2^32 / G), exact for K * G < 2^32 (checked on the host).
+  const uint32_t gmag = (uint32_t)((0x100000000ull + (uint64_t)G - 1) / (uint64_t)G);
+  auto group_of = [&](int kb) {
+    if constexpr (kLean)
+      return (int)__umulhi((uint32_t)(kb + 32 * fh), gmag);
+    else
+      return (kb + 32 * fh) / G;
+  };
 
   // Scales and zero points of the tile: S | Z << 16 per (column, group),
   // pitch gpr + 1.
@@ -167,12 +192,20 @@ __global__ __launch_bounds__(kThreads, kRing == 3 ? 2 : 1) void gemm_mid_kernel(
   };
   auto load_a = [&](ARegs& R, int kb) {
 #pragma unroll
-    for (int i = 0; i < kAUnits; ++i) R.a[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + kb);
+    for (int i = 0; i < kAUnits; ++i) {
+      if constexpr (kLean)
+        R.a[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (int)a_off[i], 2 * kb, 0));
+      else
+        R.a[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + kb);
+    }
   };
   auto load_b = [&](BRegs& R, int kb) {
-    R.w = *reinterpret_cast<const u32x4_t*>(b_src + kb / 2);
+    if constexpr (kLean)
+      R.w = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, (int)b_off, kb / 2, 0));
+    else
+      R.w = *reinterpret_cast<const u32x4_t*>(b_src + kb / 2);
     if constexpr (!SZL) {
-      const int64_t gi = g_row + (kb + 32 * fh) / G;
+      const int64_t gi = g_row + group_of(kb);
       R.s16 = scales[gi];
       R.z16 = ASYM ? zeros[gi] : (uint16_t)0;
     }
@@ -219,7 +252,7 @@ __global__ __launch_bounds__(kThreads, kRing == 3 ? 2 : 1) void gemm_mid_kernel(
     const uint16_t* base = my_stages + st * kStage;
     uint16_t s16, z16;
     if constexpr (SZL) {
-      const uint32_t v = szs[(32 * cg + fr) * szp + (kb + 32 * fh) / G];
+      const uint32_t v = szs[(32 * cg + fr) * szp + group_of(kb)];
       s16 = (uint16_t)(v & 0xFFFFu);
       z16 = (uint16_t)(v >> 16);
     } else {

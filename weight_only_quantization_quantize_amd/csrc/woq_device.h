@@ -60,6 +60,11 @@ struct BF16 {
   }
 };
 
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs, gfx950
+// included: 32-bit data format, no swizzle.  Loads past the resource's byte
+// count return zero.
+constexpr int kBufferWord3 = 0x00020000;
+
 // ---------------------------------------------------------------------------
 // Packed-code decode.  Each helper returns the code pair (k, k+1) of pair index
 // t in the two 16-bit halves, OR-ed with the magic pattern.

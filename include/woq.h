@@ -104,7 +104,7 @@ size_t woq_scales_bytes(int64_t N, int64_t K, int32_t group_size);
 
 /* Workspace bytes woq_w4a16_gemm can use for this shape (0 for invalid
  * arguments).  Non-zero (8 M bytes rounded up to 256, plus 2 M K bytes) for
- * M >= 33, 4-bit codes and K % 64 == 0: there, bf16 X given a workspace at
+ * M >= 33, 4-bit codes, K % 64 == 0 and K < 65536: there, bf16 X given a workspace at
  * least this large (256-byte aligned, device memory the call may overwrite)
  * runs on the fp16 mid-M (33..127 rows, where fp16 X would take it) or
  * register-B (M >= 128) kernel through an exact per-row power-of-two rescale:
@@ -145,7 +145,7 @@ woq_status woq_w4a16_gemv(const void* x, int32_t xdtype, const float* act_scale,
  *   X : [M, K] row-major of xdtype;  Y : out, [M, N] row-major of xdtype.
  * Small M decodes weights in registers and feeds MFMA with an exact integer
  * (u - Z) and per-group fp32 scaling.  Large M (M >= 128 and, for fp16,
- * K % 64 == 0), and fp16 X with 4-bit codes and K % 64 == 0 at 33..127 rows
+ * K % 64 == 0), and fp16 X with 4-bit codes, K % 64 == 0 and K < 65536 at 33..127 rows
  * (always above 64 rows; at 33..64 rows when N >= 16384 or the small-batch
  * kernel does not take the shape), feed MFMA with dequantized weights: for
  * fp16, w_hat rounded once to fp16 (decoded straight into operand registers

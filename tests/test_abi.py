@@ -58,7 +58,7 @@ def test_size_queries(lib):
 def test_gemm_workspace_bytes(lib):
     # bf16 rows' power-of-two factors (f_m and 1 / f_m, fp32; 8 M bytes
     # rounded up to 256) and the rescaled fp16 copy of X (2 M K bytes), only
-    # where the rescaled route exists: M >= 33, 4-bit, K % 64 == 0
+    # where the rescaled route exists: M >= 33, 4-bit, K % 64 == 0, K < 65536
     def need(M, K):
         return (8 * M + 255) // 256 * 256 + 2 * M * K
     for M, N, K in ((128, 520, 512), (300, 520, 1536), (2048, 11008, 4096), (64, 28672, 8192), (33, 520, 512)):
@@ -66,6 +66,8 @@ def test_gemm_workspace_bytes(lib):
     assert lib.woq_workspace_bytes(32, 520, 512, 4, 128) == 0
     assert lib.woq_workspace_bytes(300, 520, 1536, 3, 128) == 0
     assert lib.woq_workspace_bytes(300, 520, 1056, 4, 32) == 0
+    assert lib.woq_workspace_bytes(64, 520, 65408, 4, 128) == need(64, 65408)
+    assert lib.woq_workspace_bytes(64, 520, 65536, 4, 128) == 0
     for bad in ((0, 520, 512, 4, 128), (300, 0, 512, 4, 128), (300, 520, 500, 4, 128), (300, 520, 512, 5, 128),
                 (300, 520, 512, 4, 100), (300, 520, 512, 4, 384)):
         assert lib.woq_workspace_bytes(*bad) == 0

@@ -475,7 +475,8 @@ static bool lds_tiles_fill_chip(int64_t M, int64_t N) {
 }
 
 bool gemm_uses_regb(int64_t M, int64_t N, int64_t K, int bits, int xdtype) {
-  return M >= kLdsGemmMinM && xdtype == 0 && bits == 4 && K % 64 == 0 && !lds_tiles_fill_chip(M, N);
+  // K < 2^16: the kernel's group index by multiplication needs K * G < 2^32
+  return M >= kLdsGemmMinM && xdtype == 0 && bits == 4 && K % 64 == 0 && K < 65536 && !lds_tiles_fill_chip(M, N);
 }
 
 // The mid-M kernel (gemm_mid.hip, fp16 X, 4-bit codes, 64 x 128 tiles) takes
@@ -578,7 +579,10 @@ __global__ __launch_bounds__(kXbThreads) void xb_rescale_kernel(const uint16_t* 
 }
 
 // Shapes whose bf16 X can run on the fp16 mid-M or register-B kernel.
-bool xb_rescale_ok(int64_t M, int64_t K, int bits) { return M >= kMidMinM && bits == 4 && K % 64 == 0; }
+// (K < 2^16: both consumers index groups by multiplication, exact for K * G < 2^32.)
+bool xb_rescale_ok(int64_t M, int64_t K, int bits) {
+  return M >= kMidMinM && bits == 4 && K % 64 == 0 && K < 65536;
+}
 
 }  // namespace
 

@@ -23,7 +23,13 @@
 //     (w >> 4t) & 0x000F000F, t = 0..3.
 //   * Each pair is widened exactly, (1024 + u) - (1024 + Z) = u - Z in fp16,
 //     and multiplied by S once: the weight is the same fp16 w_hat as in the
-//     LDS-staged kernel.  With an AWQ scale, A holds x * act_recip(s) rounded
+//     LDS-staged kernel.  The pair one nibble up is OR-ed into 0x5400 (64 + u)
+//     and loses 64 + Z' = fp16(1024 + Z) - 960 instead, the same exact
+//     difference, so a code word costs one shift instead of three.
+//   * Codes and X are read through buffer resources over the tile's columns
+//     and rows (a 32-bit offset per lane, the K block's offset in a scalar
+//     register), and a lane's group index is one multiply by ceil(2^32 / G)
+//     (exact for K * G < 2^32): no address or division arithmetic per block.  With an AWQ scale, A holds x * act_recip(s) rounded
 //     once to fp16, also as there.
 //
 // The tile's scales and zero points (K / G <= 40 groups) are staged in LDS
@@ -120,16 +126,23 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
   const int fr = lane & 31, fh = lane >> 5;
   const int gpr = K / G;
   const int kblocks = K / kBK;
+  // (kb + 32 h) / G for the block at kb
+  const uint32_t gmag = (uint32_t)((0x100000000ull + (uint64_t)G - 1) / (uint64_t)G);
+  auto group_of = [&](int kb) { return (int)__umulhi((uint32_t)(kb + 32 * fh), gmag); };
 
   // A staging: thread t owns segment t % 8 of rows t / 8 + 32 i.  Rows past M
   // read row M - 1; their outputs are never stored.
   const int a_seg = tid % kASegs, a_r0 = tid / kASegs;
-  const uint16_t* a_src[kAUnits];
+  uint32_t a_off[kAUnits];  // bytes from row m0 of X
 #pragma unroll
   for (int i = 0; i < kAUnits; ++i) {
     const int r = m0 + a_r0 + kARowStep * i;
-    a_src[i] = X + (int64_t)(r < M ? r : M - 1) * K + 8 * a_seg;
+    a_off[i] = 2u * (uint32_t)(((r < M ? r : M - 1) - m0) * K + 8 * a_seg);
   }
+  const int64_t x_bytes = 2 * ((int64_t)M - m0) * K;
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X + (int64_t)m0 * K), 0,
+                                        (int)(x_bytes < 0x7FFFFFFF ? x_bytes : 0x7FFFFFFF), kBufferWord3);
   const uint32_t a_dst = (uint32_t)(a_r0 * kLD + 8 * a_seg);
   // XB: g_m of the tile's rows, in LDS (registers are at the limit of two
   // workgroups per compute unit); read only after the loop's barriers.
@@ -144,15 +157,19 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
   // B: subtile j of this wave is column n0 + 64 wave + 32 j + l%32 (columns
   // past N read column N - 1, never stored); this lane's chunk of a block
   // starting at k is codes [k + 32 h, k + 32 h + 32).
-  const uint8_t* b_src[2];
+  uint32_t b_off[2];  // bytes from column n0 of the codes
   int64_t g_row[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     int c = n0 + 64 * wave + 32 * j + fr;
     c = c < N ? c : N - 1;
-    b_src[j] = packed + (int64_t)c * (K / 2) + 16 * fh;
+    b_off[j] = (uint32_t)((c - n0) * (K / 2) + 16 * fh);
     g_row[j] = (int64_t)c * gpr;
   }
+  const int64_t b_bytes = ((int64_t)N - n0) * (K / 2);
+  const __amdgpu_buffer_rsrc_t b_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(packed + (int64_t)n0 * (K / 2)), 0,
+                                        (int)(b_bytes < 0x7FFFFFFF ? b_bytes : 0x7FFFFFFF), kBufferWord3);
 
   // SZL: the tile's scales and zero points, S | Z << 16 per (column, group)
   // with pitch gpr + 1 (conflict-free for 32 consecutive columns), loaded
@@ -206,14 +223,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
   };
   auto load_a = [&](ARegs& R, int kb) {
 #pragma unroll
-    for (int i = 0; i < kAUnits; ++i) R.a[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + kb);
+    for (int i = 0; i < kAUnits; ++i)
+      R.a[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (int)a_off[i], 2 * kb, 0));
   };
   auto load_b = [&](BRegs& R, int kb) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      R.w[j] = *reinterpret_cast<const u32x4_t*>(b_src[j] + kb / 2);
+      R.w[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, (int)b_off[j], kb / 2, 0));
       if constexpr (!SZL) {
-        const int64_t gi = g_row[j] + (kb + 32 * fh) / G;
+        const int64_t gi = g_row[j] + group_of(kb);
         R.s16[j] = scales[gi];
         R.z16[j] = ASYM ? zeros[gi] : (uint16_t)0;
       }
@@ -255,16 +273,17 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const uint32_t a_rd = (uint32_t)(fr * kLD + 32 * fh);
-  const uint32_t magic = vgpr_const(0x64006400u);  // one v_and_or_b32 per pair
+  const uint32_t magic = vgpr_const(0x64006400u);    // 1024 + u: one v_and_or_b32 per pair
+  const uint32_t magic64 = vgpr_const(0x54005400u);  // 64 + u, the pair one nibble up
   const float zsym = 8.0f;
   auto mma_block = [&](int st, const BRegs& R, int kb) {
     const uint16_t* base = lds + st * kStage;
-    uint32_t zm[2], s2[2];
+    uint32_t zm[2], zm64[2], s2[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint16_t s16, z16;
       if constexpr (SZL) {
-        const uint32_t v = szs[(64 * wave + 32 * j + fr) * szp + (kb + 32 * fh) / G];
+        const uint32_t v = szs[(64 * wave + 32 * j + fr) * szp + group_of(kb)];
         s16 = (uint16_t)(v & 0xFFFFu);
         z16 = (uint16_t)(v >> 16);
       } else {
@@ -274,6 +293,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
       const float Z = ASYM ? half_bits_to_f32(z16) : zsym;
       const uint32_t zh = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(1024.0f + Z));
       zm[j] = zh | (zh << 16);
+      zm64[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, zm[j]) - (h2_t){(_Float16)960.0f, (_Float16)960.0f});
       s2[j] = (uint32_t)s16 | ((uint32_t)s16 << 16);
     }
 #pragma unroll
@@ -283,9 +303,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
       for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4_t*>(base + a_rd + 32 * kLD * i + 8 * ks);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t w = R.w[j][ks];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) b[j][t] = dequant_pair(((w >> (4 * t)) & 0x000F000Fu) | magic, zm[j], s2[j]);
+        const uint32_t w = R.w[j][ks], w8 = w >> 8;
+        b[j][0] = dequant_pair((w & 0x000F000Fu) | magic, zm[j], s2[j]);
+        b[j][1] = dequant_pair((w & 0x00F000F0u) | magic64, zm64[j], s2[j]);
+        b[j][2] = dequant_pair((w8 & 0x000F000Fu) | magic, zm[j], s2[j]);
+        b[j][3] = dequant_pair((w8 & 0x00F000F0u) | magic64, zm64[j], s2[j]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)

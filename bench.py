@@ -41,6 +41,7 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-rows]
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -482,10 +483,14 @@ def time_rows(torch, ops, synth, checks):
     del Xg, Wg
 
     # quantize_pack over 32 layers of the LLaMA-2-7B linear shapes (weights
-    # generated on the device, seed 5100 + layer), 4-bit asym g128.
+    # generated on the device, seed 5100 + layer, all 32 layers resident:
+    # 13 GB of fp16), 4-bit asym g128: one woq_quantize_pack call per matrix,
+    # each layer's 7 back to back; then woq_quantize_pack_many over all 224
+    # matrices (32 per launch) into a second set of outputs.
     shapes = [(N, K) for _, N, K in synth.LLAMA7B_LINEARS]
     total_bytes, total_us = 0, 0.0
     g = torch.Generator(device=dev)
+    layers = []
     for layer in range(32):
         g.manual_seed(5100 + layer)
         Ws = [(torch.randn(N, K, generator=g, device=dev) * 0.02).half() for N, K in shapes]
@@ -496,10 +501,33 @@ def time_rows(torch, ops, synth, checks):
         if layer == 0:
             checks.append(("quantize_pack", "quantize_pack_32_layers", "sampled_bytes_equal",
                            Ws[0][:256].cpu().numpy(), tuple(t[:256].cpu().numpy() for t in outs[0])))
-        del Ws, outs
-    rows["quantize_pack_32_layers"] = {"ms": round(total_us / 1e3, 3), "bytes": total_bytes,
-                                       "gbs": round(total_bytes / total_us / 1e3, 1),
-                                       "frac_hbm": round(total_bytes / total_us / 1e3 / HBM_PEAK_GBS, 4)}
+        layers.append(Ws)
+        del outs
+    all_W = [w for Ws in layers for w in Ws]
+    many_outs = [(torch.empty((w.shape[0], w.shape[1] // 2), dtype=torch.uint8, device=dev),
+                  torch.empty((w.shape[0], w.shape[1] // 128), dtype=torch.float16, device=dev),
+                  torch.empty((w.shape[0], w.shape[1] // 128), dtype=torch.float16, device=dev)) for w in all_W]
+    ops.quantize_pack_many(all_W, 4, 128, True, None, many_outs)  # validated once through the binding
+    from weight_only_quantization_quantize_amd import _lib
+    lib, stream = _lib.load(), torch.cuda.current_stream().cuda_stream
+    descs = (_lib.QMatrix * len(all_W))(*[
+        _lib.QMatrix(w.data_ptr(), None, p.data_ptr(), sc.data_ptr(), z.data_ptr(), w.shape[0], w.shape[1])
+        for w, (p, sc, z) in zip(all_W, many_outs)])
+
+    def many():
+        _lib.check(lib.woq_quantize_pack_many(ctypes.addressof(descs), len(all_W), 4, 128, 1, stream),
+                   "woq_quantize_pack_many")
+
+    many_us = burst_us(torch, [many], reps=2)
+    checks.append(("quantize_pack", "quantize_pack_32_layers", "many_sampled_bytes_equal",
+                   all_W[0][:256].cpu().numpy(), tuple(t[:256].cpu().numpy() for t in many_outs[0])))
+    del layers, all_W, many_outs
+    rows["quantize_pack_32_layers"] = {
+        "ms": round(total_us / 1e3, 3), "bytes": total_bytes, "gbs": round(total_bytes / total_us / 1e3, 1),
+        "frac_hbm": round(total_bytes / total_us / 1e3 / HBM_PEAK_GBS, 4),
+        "many": {"ms": round(many_us / 1e3, 3), "launches": -(-224 // 32),
+                 "gbs": round(total_bytes / many_us / 1e3, 1),
+                 "frac_hbm": round(total_bytes / many_us / 1e3 / HBM_PEAK_GBS, 4)}}
     return rows
 
 

@@ -127,6 +127,34 @@ woq_status woq_quantize_pack(const void* W, const float* act_scale, int64_t N, i
                              int32_t bits, int32_t group_size, int32_t asymmetric,
                              void* packed, void* scales, void* zeros, void* stream);
 
+/* One matrix of woq_quantize_pack_many: the per-matrix arguments of
+ * woq_quantize_pack (device pointers owned by the caller). */
+typedef struct woq_qmatrix {
+  const void* W;          /* fp16 [N, K] */
+  const float* act_scale; /* fp32 [K] or NULL, per matrix */
+  void* packed;           /* out, uint8 [N, K*bits/8] in layout v2 */
+  void* scales;           /* out, fp16 [N, K/group_size] */
+  void* zeros;            /* out, fp16 [N, K/group_size] when asymmetric, else NULL */
+  int64_t N, K;
+} woq_qmatrix;
+
+/* woq_quantize_pack over `count` matrices that share bits, group_size and
+ * asymmetric -- e.g. every linear of a model, which a model conversion
+ * quantizes and packs once, offline ("MIT 6.5940 Lab 4 + Lab 5", section
+ * "Background: why the 4-bit weights get reordered first").  Each matrix's
+ * packed, scales and zeros are byte-equal to what woq_quantize_pack writes
+ * for the same arguments.  When group_size / 32 divides 64 up to 32 matrices
+ * share one launch, so one matrix's tail overlaps the next one's start;
+ * other group sizes take one launch per matrix.
+ *   mats  : HOST array of `count` descriptors (count >= 1), read during the
+ *           call only.
+ * Every descriptor is checked as woq_quantize_pack checks its arguments
+ * before anything is enqueued; an invalid one fails the whole call with
+ * WOQ_ERR_INVALID_ARGUMENT and woq_last_error() names its index.  Outputs
+ * of different matrices must not overlap one another or any input. */
+woq_status woq_quantize_pack_many(const woq_qmatrix* mats, int32_t count, int32_t bits, int32_t group_size,
+                                  int32_t asymmetric, void* stream);
+
 /* y[n] = sum_k (x[k] / s[k]) * w_hat[n, k]  (M = 1 decode GEMV).
  *   x         : [K] of xdtype (WOQ_F16 or WOQ_BF16)
  *   act_scale : fp32 [K] (the same s given to woq_quantize_pack) or NULL

@@ -4,6 +4,7 @@ queries are right, and every invalid argument is rejected before any HIP call.
 No test here launches a kernel: each call passes at least one invalid
 argument, so the library returns during validation.
 """
+import ctypes
 import os
 import re
 
@@ -33,7 +34,7 @@ def test_header_declares_the_boundary():
     for n in ("woq_quantize_pack", "woq_w4a16_gemv", "woq_w4a16_gemm", "woq_packed_bytes", "woq_workspace_bytes",
               "woq_status_string", "woq_last_error", "woq_dequantize", "woq_scales_bytes", "woq_layout_version",
               "woq_awq_search", "woq_awq_search_workspace_bytes", "woq_gptq_quantize_pack",
-              "woq_gptq_workspace_bytes"):
+              "woq_gptq_workspace_bytes", "woq_quantize_pack_many"):
         assert n in names
 
 
@@ -118,6 +119,48 @@ def _qp(lib, **kw):
 def test_quantize_pack_rejects(lib, kw, needle):
     assert _qp(lib, **kw) == _lib.WOQ_ERR_INVALID_ARGUMENT
     assert needle in lib.woq_last_error().decode()
+
+
+def _qp_many(lib, bad_index=None, bad=None, count=3, bits=4, G=128, asym=1):
+    mats = (_lib.QMatrix * max(count, 1))()
+    for i in range(max(count, 1)):
+        d = dict(W=FAKE, act_scale=None, packed=FAKE, scales=FAKE, zeros=FAKE if asym else None, N=64, K=256)
+        if i == bad_index:
+            d.update(bad)
+        mats[i] = _lib.QMatrix(**d)
+    return lib.woq_quantize_pack_many(ctypes.addressof(mats), count, bits, G, asym, None)
+
+
+@pytest.mark.parametrize(
+    "bad, needle",
+    [
+        (dict(N=0), "N must"),
+        (dict(K=100), "K must"),
+        (dict(W=None), "W must"),
+        (dict(W=FAKE + 2), "W must be 16-byte"),
+        (dict(packed=FAKE + 4), "packed must be 16-byte"),
+        (dict(scales=None), "scales"),
+        (dict(zeros=None), "zeros must not be NULL"),
+        (dict(act_scale=FAKE + 4), "act_scale"),
+    ],
+)
+def test_quantize_pack_many_rejects_a_bad_matrix_and_names_it(lib, bad, needle):
+    # the third descriptor is bad: nothing is launched and the message names it
+    assert _qp_many(lib, 2, bad) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    msg = lib.woq_last_error().decode()
+    assert "matrix 2" in msg and needle in msg, msg
+
+
+def test_quantize_pack_many_rejects_bad_calls(lib):
+    assert lib.woq_quantize_pack_many(None, 1, 4, 128, 1, None) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    assert "mats" in lib.woq_last_error().decode()
+    assert _qp_many(lib, count=0) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    assert "count" in lib.woq_last_error().decode()
+    assert _qp_many(lib, bits=5) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    assert _qp_many(lib, G=48) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    # symmetric calls take no zeros
+    assert _qp_many(lib, 0, dict(zeros=FAKE), asym=0) == _lib.WOQ_ERR_INVALID_ARGUMENT
+    assert "zeros must be NULL" in lib.woq_last_error().decode()
 
 
 def _gemv(lib, **kw):

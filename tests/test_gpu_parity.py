@@ -207,6 +207,50 @@ def test_quantize_pack_leaves_memory_past_the_outputs_untouched():
     assert torch.all(scales[N * K // 128:] == 7.0) and torch.all(zeros[N * K // 128:] == 7.0)
 
 
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("G", [128, 32, 96])
+def test_quantize_pack_many_matches_oracle(bits, asym, G):
+    # Ragged shapes in one call, with and without an AWQ scale; G = 96 takes
+    # the one-launch-per-matrix route, the others share launches.
+    rng = np.random.default_rng(700 + bits * 10 + G + asym)
+    shapes = [(37, 4 * G), (1, G), (300, 8 * G), (129, 2 * G), (64, 12 * G)]
+    Ws = [(rng.standard_normal(sh).astype(np.float32) * 0.02).astype(np.float16) for sh in shapes]
+    ss = [None if i % 2 else (rng.random(sh[1]).astype(np.float32) + 0.5) for i, sh in enumerate(shapes)]
+    _say(f"quantize_pack_many bits={bits} asym={asym} G={G}: {shapes}")
+    outs = ops.quantize_pack_many([gpu_f16(W) for W in Ws], bits, G, asym, [gpu_f32(s) for s in ss])
+    for W, s, out in zip(Ws, ss, outs):
+        assert_pack_equal(out, O.quantize_pack(W, bits, G, asym, s))
+
+
+def test_quantize_pack_many_across_launches_equals_single_calls():
+    # 40 matrices: more than one launch's worth of descriptors; each result
+    # byte-equal to its own woq_quantize_pack call, and nothing written past
+    # any output.
+    rng = np.random.default_rng(41)
+    Ws, outs, refs, guards = [], [], [], []
+    for i in range(40):
+        N, K = int(rng.integers(1, 70)), 128 * int(rng.integers(1, 9))
+        W = gpu_f16((rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16))
+        Ws.append(W)
+        refs.append(ops.quantize_pack(W, 4, 128, True))
+        pk = torch.full((N * K // 2 + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+        sc = torch.full((N * K // 128 + 32,), 7.0, dtype=torch.float16, device=DEV)
+        zr = torch.full((N * K // 128 + 32,), 7.0, dtype=torch.float16, device=DEV)
+        guards.append((pk, sc, zr, N * K // 2, N * K // 128))
+        outs.append((pk[: N * K // 2].view(N, K // 2), sc[: N * K // 128].view(N, K // 128),
+                     zr[: N * K // 128].view(N, K // 128)))
+    _say("quantize_pack_many: 40 matrices")
+    ops.quantize_pack_many(Ws, 4, 128, True, None, outs)
+    torch.cuda.synchronize()
+    for i, (out, ref, g) in enumerate(zip(outs, refs, guards)):
+        for a, b in zip(out, ref):
+            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.uint8 else a.view(torch.int16),
+                               b.view(torch.uint8) if b.dtype == torch.uint8 else b.view(torch.int16)), i
+        pk, sc, zr, nb, ns = g
+        assert torch.all(pk[nb:] == 0xA5) and torch.all(sc[ns:] == 7.0) and torch.all(zr[ns:] == 7.0), i
+
+
 # ---------------------------------------------------------------------------
 # dequantize and the layout decode
 # ---------------------------------------------------------------------------

@@ -24,6 +24,13 @@ WOQ_LAYOUT_V2 = 2
 
 _i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
+
+class QMatrix(ctypes.Structure):
+    """woq_qmatrix: one matrix of woq_quantize_pack_many."""
+    _fields_ = [("W", _vp), ("act_scale", _vp), ("packed", _vp), ("scales", _vp), ("zeros", _vp), ("N", _i64),
+                ("K", _i64)]
+
+
 # name -> (restype, argtypes); mirrors include/woq.h
 SIGNATURES = {
     "woq_layout_version": (_i32, []),
@@ -31,6 +38,7 @@ SIGNATURES = {
     "woq_scales_bytes": (_sz, [_i64, _i64, _i32]),
     "woq_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32]),
     "woq_quantize_pack": (_i32, [_vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "woq_quantize_pack_many": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp]),
     "woq_w4a16_gemv": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "woq_w4a16_gemm": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _sz,
                               _vp]),

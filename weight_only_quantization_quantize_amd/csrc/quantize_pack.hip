@@ -59,16 +59,32 @@ __device__ inline void load_chunk(const uint16_t* __restrict__ W, const float* _
   }
 }
 
-// Group of `team` consecutive chunk threads (team = G/32 divides 64).
+// Chunk c of a matrix, in a group of `team` consecutive chunk threads
+// (team = G/32 divides 64).
 template <int BITS, bool ASYM, bool FOLD>
-__global__ __launch_bounds__(kThreads) void quantize_pack_team_kernel(
-    const uint16_t* __restrict__ W, const float* __restrict__ s, int64_t total_chunks, int K, int G, int team,
-    uint8_t* __restrict__ packed, uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
-  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+__device__ __attribute__((always_inline)) inline void team_chunk(const uint16_t* __restrict__ W,
+                                                                 const float* __restrict__ s, int64_t c,
+                                                                 int64_t total_chunks, int K, int G, int team,
+                                                                 uint8_t* __restrict__ packed,
+                                                                 uint16_t* __restrict__ scales,
+                                                                 uint16_t* __restrict__ zeros) {
   const bool valid = c < total_chunks;
   const int cpr = K >> 5;
-  const int64_t n = valid ? c / cpr : 0;
-  const int kc = valid ? (int)(c - n * cpr) : 0;
+  // Row and chunk within the row: a 32-bit division whenever the matrix has
+  // fewer than 2^32 chunks (the 64-bit one cost about 60 VALU and as many
+  // scalar instructions per thread, two per weight).
+  int64_t n = 0;
+  int kc = 0;
+  if (valid) {
+    if (total_chunks <= 0xFFFFFFFFll) {
+      const uint32_t c32 = (uint32_t)c, n32 = c32 / (uint32_t)cpr;
+      n = n32;
+      kc = (int)(c32 - n32 * (uint32_t)cpr);
+    } else {
+      n = c / cpr;
+      kc = (int)(c - n * cpr);
+    }
+  }
   float w[32];
   if (valid) {
     load_chunk<FOLD>(W, s, n * (int64_t)K, kc * 32, w);
@@ -102,6 +118,74 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_team_kernel(
     scales[gi] = p.S16;
     if (ASYM) zeros[gi] = f32_to_half_bits((float)p.Z);
   }
+}
+
+template <int BITS, bool ASYM, bool FOLD>
+__global__ __launch_bounds__(kThreads) void quantize_pack_team_kernel(
+    const uint16_t* __restrict__ W, const float* __restrict__ s, int64_t total_chunks, int K, int G, int team,
+    uint8_t* __restrict__ packed, uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
+  team_chunk<BITS, ASYM, FOLD>(W, s, (int64_t)blockIdx.x * kThreads + threadIdx.x, total_chunks, K, G, team,
+                               packed, scales, zeros);
+}
+
+// Several matrices in one launch: workgroups [block0[i], block0[i + 1]) run
+// matrix i's chunks exactly as quantize_pack_team_kernel would, so matrix
+// i + 1 starts streaming while matrix i's last workgroups finish instead of
+// behind a launch boundary.  The descriptors travel in the kernel arguments
+// (indexed in place, no copy).
+struct QpManyArgs {
+  const uint16_t* W[kQpManyMax];
+  const float* s[kQpManyMax];
+  uint8_t* packed[kQpManyMax];
+  uint16_t* scales[kQpManyMax];
+  uint16_t* zeros[kQpManyMax];
+  int64_t chunks[kQpManyMax];
+  int K[kQpManyMax];
+  unsigned block0[kQpManyMax + 1];
+  int count;
+};
+
+template <int BITS, bool ASYM>
+__global__ __launch_bounds__(kThreads) void quantize_pack_many_kernel(const QpManyArgs a, int G, int team) {
+  const unsigned b = blockIdx.x;
+  int i = 0;  // the last matrix whose first workgroup is at or before b (wave-uniform)
+  for (int j = 1; j < a.count; ++j) i = a.block0[j] <= b ? j : i;
+  const int64_t c = (int64_t)(b - a.block0[i]) * kThreads + threadIdx.x;
+  if (a.s[i])
+    team_chunk<BITS, ASYM, true>(a.W[i], a.s[i], c, a.chunks[i], a.K[i], G, team, a.packed[i], a.scales[i],
+                                 a.zeros[i]);
+  else
+    team_chunk<BITS, ASYM, false>(a.W[i], nullptr, c, a.chunks[i], a.K[i], G, team, a.packed[i], a.scales[i],
+                                  a.zeros[i]);
+}
+
+template <int BITS, bool ASYM>
+hipError_t launch_many_typed(const QpMatrix* mats, int count, int G, hipStream_t stream) {
+  const int team = G / 32;
+  for (int first = 0; first < count; first += kQpManyMax) {
+    QpManyArgs a{};
+    a.count = count - first < kQpManyMax ? count - first : kQpManyMax;
+    int64_t blocks = 0;
+    for (int i = 0; i < a.count; ++i) {
+      const QpMatrix& m = mats[first + i];
+      a.W[i] = static_cast<const uint16_t*>(m.W);
+      a.s[i] = m.s;
+      a.packed[i] = static_cast<uint8_t*>(m.packed);
+      a.scales[i] = static_cast<uint16_t*>(m.scales);
+      a.zeros[i] = static_cast<uint16_t*>(m.zeros);
+      a.chunks[i] = m.N * (m.K / 32);
+      a.K[i] = (int)m.K;
+      a.block0[i] = (unsigned)blocks;
+      blocks += (a.chunks[i] + kThreads - 1) / kThreads;
+      if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    }
+    a.block0[a.count] = (unsigned)blocks;
+    hipLaunchKernelGGL((quantize_pack_many_kernel<BITS, ASYM>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a,
+                       G, team);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // One workgroup per group (any G that is a multiple of 32).
@@ -197,6 +281,30 @@ hipError_t launch_fold(const void* W, const float* s, int64_t N, int64_t K, int 
 }
 
 }  // namespace
+
+bool quantize_pack_many_batched(int group_size) {
+  const int team = group_size / 32;
+  return team <= 64 && 64 % team == 0;
+}
+
+hipError_t launch_quantize_pack_many(const QpMatrix* mats, int count, int bits, int group_size, bool asymmetric,
+                                     hipStream_t stream) {
+  if (!quantize_pack_many_batched(group_size)) {
+    // group sizes of the one-workgroup-per-group kernel: one launch each
+    for (int i = 0; i < count; ++i) {
+      const QpMatrix& m = mats[i];
+      const hipError_t e =
+          launch_quantize_pack(m.W, m.s, m.N, m.K, bits, group_size, asymmetric, m.packed, m.scales, m.zeros, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  if (bits == 4)
+    return asymmetric ? launch_many_typed<4, true>(mats, count, group_size, stream)
+                      : launch_many_typed<4, false>(mats, count, group_size, stream);
+  return asymmetric ? launch_many_typed<3, true>(mats, count, group_size, stream)
+                    : launch_many_typed<3, false>(mats, count, group_size, stream);
+}
 
 hipError_t launch_quantize_pack(const void* W, const float* act_scale, int64_t N, int64_t K, int bits,
                                 int group_size, bool asymmetric, void* packed, void* scales, void* zeros,

@@ -78,18 +78,17 @@ __device__ inline GroupParams<BITS, ASYM> group_params(float lo, float hi) {
   return p;
 }
 
-// Code of one weight: u = clip(rne(w / S), ...) (+ 2^(b-1) or + Z).
+// Code of one weight: u = clip(rne(w / S) + Z, 0, 2^b - 1) (symmetric:
+// Z = 2^(b-1), the same as clipping rne(w / S) to [-2^(b-1), 2^(b-1) - 1]
+// and adding 2^(b-1)).  S == 0 needs no branch: R = 0 makes the quotient 0
+// for finite w, so u = clip(Z) = Z, the definition's code for that group.
+// (A branch per weight compiled to an exec-mask change around each of a
+// chunk's 32 codes.)  The float -> int conversion saturates, so quotients
+// of any size clip as the definition says.
 template <int BITS, bool ASYM>
 __device__ inline uint32_t code_of(float w, const GroupParams<BITS, ASYM>& p) {
-  if (p.zero) return (uint32_t)p.Z;
-  int q = (int)__builtin_rintf(div_by_scale(w, p.S, p.R));
-  if (!ASYM) {
-    const int h = 1 << (BITS - 1);
-    q = q < -h ? -h : (q > h - 1 ? h - 1 : q);
-    return (uint32_t)(q + h);
-  }
+  const int v = (int)__builtin_rintf(div_by_scale(w, p.S, p.R)) + p.Z;
   const int top = (1 << BITS) - 1;
-  const int v = q + p.Z;
   return (uint32_t)(v < 0 ? 0 : (v > top ? top : v));
 }
 

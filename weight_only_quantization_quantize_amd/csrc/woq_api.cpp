@@ -9,6 +9,7 @@
 #include <cstring>
 #include <exception>
 #include <string>
+#include <vector>
 
 #include "woq_internal.h"
 
@@ -161,6 +162,28 @@ woq_status woq_quantize_pack(const void* W, const float* act_scale, int64_t N, i
   return from_hip(woq::launch_quantize_pack(W, act_scale, N, K, bits, group_size, asymmetric != 0, packed, scales,
                                             zeros, static_cast<hipStream_t>(stream)),
                   "quantize_pack launch");
+  WOQ_GUARD_END
+}
+
+woq_status woq_quantize_pack_many(const woq_qmatrix* mats, int32_t count, int32_t bits, int32_t group_size,
+                                  int32_t asymmetric, void* stream) {
+  WOQ_GUARD_BEGIN
+  if (!mats) return fail(WOQ_ERR_INVALID_ARGUMENT, "mats must not be NULL");
+  if (count < 1) return fail(WOQ_ERR_INVALID_ARGUMENT, "count must be >= 1 (got %d)", count);
+  std::vector<woq::QpMatrix> qm((size_t)count);
+  for (int32_t i = 0; i < count; ++i) {
+    const woq_qmatrix& m = mats[i];
+    woq_status st = check_qparams(m.N, m.K, bits, group_size);
+    if (st == WOQ_OK && !m.W) st = fail(WOQ_ERR_INVALID_ARGUMENT, "W must not be NULL");
+    if (st == WOQ_OK && !aligned(m.W, 16)) st = fail(WOQ_ERR_INVALID_ARGUMENT, "W must be 16-byte aligned");
+    if (st == WOQ_OK) st = check_packed_inputs(m.packed, m.scales, m.zeros, asymmetric);
+    if (st == WOQ_OK) st = check_act_scale(m.act_scale);
+    if (st != WOQ_OK) return fail(st, "matrix %d: %s", i, g_last_error.c_str());
+    qm[(size_t)i] = woq::QpMatrix{m.W, m.act_scale, m.packed, m.scales, m.zeros, m.N, m.K};
+  }
+  return from_hip(woq::launch_quantize_pack_many(qm.data(), count, bits, group_size, asymmetric != 0,
+                                                 static_cast<hipStream_t>(stream)),
+                  "quantize_pack_many launch");
   WOQ_GUARD_END
 }
 

@@ -14,6 +14,22 @@ hipError_t launch_quantize_pack(const void* W, const float* act_scale, int64_t N
                                 int group_size, bool asymmetric, void* packed, void* scales, void* zeros,
                                 hipStream_t stream);
 
+// Several matrices sharing bits, group size and symmetry: up to kQpManyMax
+// per launch when the group size suits the chunk-team kernel (G / 32 divides
+// 64), otherwise one launch per matrix.
+constexpr int kQpManyMax = 32;
+struct QpMatrix {
+  const void* W;
+  const float* s;
+  void* packed;
+  void* scales;
+  void* zeros;
+  int64_t N, K;
+};
+bool quantize_pack_many_batched(int group_size);
+hipError_t launch_quantize_pack_many(const QpMatrix* mats, int count, int bits, int group_size, bool asymmetric,
+                                     hipStream_t stream);
+
 // M = 1 GEMV.  xdtype: 0 = fp16, 1 = bf16.
 hipError_t launch_gemv(const void* x, int xdtype, const float* act_scale, const void* packed,
                        const void* scales, const void* zeros, int64_t N, int64_t K, int bits,

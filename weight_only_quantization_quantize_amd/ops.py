@@ -6,6 +6,7 @@ library.  Nothing is computed here.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional, Sequence, Tuple
 
 import torch
@@ -204,6 +205,52 @@ def dequantize(
     return out
 
 
+def quantize_pack_many(
+    Ws: Sequence[torch.Tensor],
+    bits: int = 4,
+    group_size: int = 128,
+    asymmetric: bool = True,
+    act_scales: Optional[Sequence[Optional[torch.Tensor]]] = None,
+    outs: Optional[Sequence[Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]]] = None,
+):
+    """quantize_pack over several fp16 matrices [N_i, K_i] that share bits,
+    group_size and asymmetric, through woq_quantize_pack_many (up to 32
+    matrices per launch).  act_scales[i] (or None) is matrix i's AWQ scale;
+    outs[i], if given, its (packed, scales, zeros | None).  Returns one
+    (packed, scales, zeros | None) per matrix, byte-equal to quantize_pack's."""
+    if not Ws:
+        raise ValueError("need at least one matrix")
+    if act_scales is not None and len(act_scales) != len(Ws):
+        raise ValueError("act_scales must have one entry per matrix")
+    if outs is not None and len(outs) != len(Ws):
+        raise ValueError("outs must have one entry per matrix")
+    results = []
+    descs = (_lib.QMatrix * len(Ws))()
+    for i, W in enumerate(Ws):
+        if W.dtype != torch.float16 or W.dim() != 2:
+            raise ValueError(f"matrix {i}: W must be a 2-D float16 tensor")
+        N, K = W.shape
+        _check_quantizer(N, K, bits, group_size)
+        s = None if act_scales is None else act_scales[i]
+        _check_act_scale(s, K)
+        if outs is None:
+            packed = torch.empty((N, K * bits // 8), dtype=torch.uint8, device=W.device)
+            scales = torch.empty((N, K // group_size), dtype=torch.float16, device=W.device)
+            zeros = torch.empty_like(scales) if asymmetric else None
+        else:
+            packed, scales, zeros = outs[i]
+            if (zeros is not None) != bool(asymmetric):
+                raise ValueError(f"matrix {i}: out must hold zeros exactly when asymmetric")
+            _check_packed(packed, scales, zeros, N, K, bits, group_size)
+        _require_gpu(Ws[0], W, s, packed, scales, zeros)
+        descs[i] = _lib.QMatrix(W.data_ptr(), _ptr(s), packed.data_ptr(), scales.data_ptr(), _ptr(zeros), N, K)
+        results.append((packed, scales, zeros))
+    st = _lib.call("woq_quantize_pack_many", ctypes.addressof(descs), len(Ws), bits, group_size, int(asymmetric),
+                   _stream(Ws[0]))
+    _lib.check(st, "woq_quantize_pack_many")
+    return results
+
+
 def quantize_pack_fused(
     Ws: Sequence[torch.Tensor],
     bits: int = 4,
@@ -214,7 +261,7 @@ def quantize_pack_fused(
     """Quantize several weight matrices that read the same input (q/k/v, or
     gate/up) into one packed set whose rows are theirs, stacked: matrix i
     fills rows [sum(N_<i), sum(N_<=i)) of each output, written in place by one
-    woq_quantize_pack call per matrix.  A single gemv/gemm over N = sum(N_i)
+    woq_quantize_pack_many call.  A single gemv/gemm over N = sum(N_i)
     then serves all of them.  Returns (packed, scales, zeros | None, sizes)."""
     if not Ws:
         raise ValueError("need at least one matrix")
@@ -227,11 +274,11 @@ def quantize_pack_fused(
     packed = torch.empty((N, packed_bytes(1, K, bits)), dtype=torch.uint8, device=dev)
     scales = torch.empty((N, K // group_size), dtype=torch.float16, device=dev)
     zeros = torch.empty_like(scales) if asymmetric else None
-    row = 0
-    for W, n in zip(Ws, sizes):
-        quantize_pack(W, bits, group_size, asymmetric, act_scale,
-                      out=(packed[row:row + n], scales[row:row + n], None if zeros is None else zeros[row:row + n]))
+    outs, row = [], 0
+    for n in sizes:
+        outs.append((packed[row:row + n], scales[row:row + n], None if zeros is None else zeros[row:row + n]))
         row += n
+    quantize_pack_many(Ws, bits, group_size, asymmetric, [act_scale] * len(Ws), outs)
     return packed, scales, zeros, sizes
 
 

@@ -111,7 +111,7 @@ __device__ __attribute__((always_inline)) inline void team_chunk(const uint16_t*
   if (!valid) return;
   const GroupParams<BITS, ASYM> p = group_params<BITS, ASYM>(lo, hi);
   uint32_t u[32];
-  codes_of_chunk<BITS, ASYM>(w, p, u);
+  codes_of_chunk<BITS, ASYM, !FOLD>(w, p, u);
   store_chunk<BITS>(packed, n, K, kc, u);
   if ((kc & (team - 1)) == 0) {
     const int64_t gi = n * (int64_t)(K / G) + (kc * 32) / G;
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_block_kernel(
     float w[32];
     load_chunk<FOLD>(W, s, n * (int64_t)K, (c0 + c) * 32, w);
     uint32_t u[32];
-    codes_of_chunk<BITS, ASYM>(w, p, u);
+    codes_of_chunk<BITS, ASYM, !FOLD>(w, p, u);
     store_chunk<BITS>(packed, n, K, c0 + c, u);
   }
   if (threadIdx.x == 0) {

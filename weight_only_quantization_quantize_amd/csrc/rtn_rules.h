@@ -46,6 +46,24 @@ __device__ inline float div_by_scale(float w, float S, float R) {
   return __builtin_fmaf(__builtin_fmaf(-q1, S, w), R, q1);
 }
 
+// The same code with one correction step, for fp16 w (no AWQ fold) and
+// fp16 S.  Only |w / S| < 16 can give a code that is not clipped, and there
+// w / S is either
+//  * exactly a half-integer h: q0 = h (1 + e) with |e| <= 2^-23, the residual
+//    w - q0 S = -h e S is exact, and q0 + R (-h e S) = h up to h 2^-46, so
+//    the corrected quotient is h itself, as the IEEE quotient is; or
+//  * at least 2^-12 away from every half-integer: 2 w - (2k + 1) S is a
+//    nonzero integer multiple of 2^min(e_w + 1, e_S), e_w and e_S being the
+//    weights of the last significand bits of w and S, and S < 2^(e_S + 11);
+//    the corrected quotient is within an ulp (2^-19 below 16) of w / S, so it
+//    rounds to the same integer as the IEEE quotient.
+// tests/test_quantize_rounding.py checks the gap on every fp16 w against
+// fp16 scales of every binade.
+__device__ inline float div_by_scale_f16(float w, float S, float R) {
+  const float q0 = w * R;
+  return __builtin_fmaf(__builtin_fmaf(-q0, S, w), R, q0);
+}
+
 template <int BITS, bool ASYM>
 __device__ inline void set_reciprocal(GroupParams<BITS, ASYM>& p) {
   p.R = p.zero ? 0.0f : 1.0f / p.S;
@@ -85,17 +103,20 @@ __device__ inline GroupParams<BITS, ASYM> group_params(float lo, float hi) {
 // (A branch per weight compiled to an exec-mask change around each of a
 // chunk's 32 codes.)  The float -> int conversion saturates, so quotients
 // of any size clip as the definition says.
-template <int BITS, bool ASYM>
+// F16W: w is an fp16 value (no fold), so one correction step decides the
+// same code (div_by_scale_f16).
+template <int BITS, bool ASYM, bool F16W = false>
 __device__ inline uint32_t code_of(float w, const GroupParams<BITS, ASYM>& p) {
-  const int v = (int)__builtin_rintf(div_by_scale(w, p.S, p.R)) + p.Z;
+  const float q = F16W ? div_by_scale_f16(w, p.S, p.R) : div_by_scale(w, p.S, p.R);
+  const int v = (int)__builtin_rintf(q) + p.Z;
   const int top = (1 << BITS) - 1;
   return (uint32_t)(v < 0 ? 0 : (v > top ? top : v));
 }
 
-template <int BITS, bool ASYM>
+template <int BITS, bool ASYM, bool F16W = false>
 __device__ inline void codes_of_chunk(const float (&w)[32], const GroupParams<BITS, ASYM>& p, uint32_t (&u)[32]) {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) u[i] = code_of<BITS, ASYM>(w[i], p);
+  for (int i = 0; i < 32; ++i) u[i] = code_of<BITS, ASYM, F16W>(w[i], p);
 }
 
 template <int BITS>

@@ -54,7 +54,7 @@ constexpr int kTargetWaves = WOQ_GEMV_WAVES;  // waves per workgroup
 #define WOQ_GEMV_PREFETCH 2
 #endif
 constexpr int kTargetBlocks = WOQ_GEMV_BLOCKS;   // workgroups sweeping the matrix together
-constexpr int kMaxSteps = WOQ_GEMV_MAXSTEPS;     // row steps per workgroup (at most; twice that on the general path)
+constexpr int kMaxSteps = WOQ_GEMV_MAXSTEPS;     // row steps per workgroup (at most; 2x / 4x on the general path)
 constexpr int kPrefetch = WOQ_GEMV_PREFETCH;     // steps of code loads in flight ahead of compute
 
 struct __attribute__((packed, aligned(4))) U32x3 {
@@ -400,8 +400,13 @@ hipError_t launch_scale(const void* x, const float* s, const void* packed, const
   const int64_t groups = (N + rpb - 1) / rpb;
   int steps = 1;
   // The general path's lanes do more per step (run-time shape), so it takes up
-  // to twice as many steps per workgroup (measured: K = 11008 12.3 -> 10.9 us).
-  const int max_steps = fixed_shape(K, G) ? kMaxSteps : 2 * kMaxSteps;
+  // to twice as many steps per workgroup (measured: K = 11008 12.3 -> 10.9 us),
+  // and four times as many with an AWQ scale, whose x staging (x and the fp32
+  // s, one reciprocal per activation) every workgroup repeats: LLaMA-2-7B down
+  // projection (K = 11008) 9.0 -> 8.35 us at 256 workgroups of 16 steps.
+  // Without the scale, and on the fixed shapes (gate / up 6.88 -> 7.18 us),
+  // more steps were slower.
+  const int max_steps = fixed_shape(K, G) ? kMaxSteps : (SCALE ? 4 : 2) * kMaxSteps;
   while (steps < max_steps && groups / (2 * steps) >= kTargetBlocks) steps *= 2;
   const int64_t blocks = (groups + steps - 1) / steps;
   switch (steps) {
@@ -413,10 +418,8 @@ hipError_t launch_scale(const void* x, const float* s, const void* packed, const
       return launch_steps<BITS, ASYM, XT, SCALE, 4>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, y, stream);
     case 8:
       return launch_steps<BITS, ASYM, XT, SCALE, 8>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, y, stream);
-#if WOQ_GEMV_MAXSTEPS >= 16
     case 16:
       return launch_steps<BITS, ASYM, XT, SCALE, 16>(x, s, packed, scales, zeros, N, K, G, spr, rpb, blocks, y, stream);
-#endif
     default:
       return hipErrorInvalidValue;
   }

@@ -415,6 +415,21 @@ def test_gemm_small_shapes(M, xdtype):
     gemm_case(W, X, xdtype, 4, False, label="small")
 
 
+@pytest.mark.parametrize("M", [64, 96, 160])
+@pytest.mark.parametrize("K", [65408, 65536])
+def test_gemm_longest_rows_take_the_right_kernels(M, K):
+    # The mid-M and register-B kernels index groups by multiplying with
+    # ceil(2^32 / G), exact for K * G < 2^32, so they take K < 65536: 65408
+    # runs on them, 65536 on the kernels that divide.  Both agree with the
+    # oracle; the bf16 route with a workspace follows the same rule.
+    rng = np.random.default_rng(M + K)
+    N = 72
+    W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
+    X32 = rng.standard_normal((M, K)).astype(np.float32)
+    gemm_case(W, X32.astype(np.float16), "f16", 4, True, label="long rows")
+    gemm_case(W, synth.to_bf16_bits(X32), "bf16", 4, True, label="long rows")
+
+
 @pytest.mark.parametrize("G", [32, 64, 256])
 def test_gemm_group_sizes(G):
     rng = np.random.default_rng(G + 1)

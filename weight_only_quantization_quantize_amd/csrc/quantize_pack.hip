@@ -15,15 +15,18 @@
 // Every decision is one correctly rounded binary32 operation: the quotient
 // of IEEE division (the group's S / qmax and -min / S divide; a weight's w / S
 // comes from the group's reciprocal with two exact fma corrections, equal to
-// the IEEE quotient), rintf = round half to even, fp32 -> fp16 conversion
-// round-to-nearest-even with subnormals, and no FMA contraction in this file.
+// the IEEE quotient, or with one when w is an unfolded fp16 weight, which
+// rounds to the same integer; rtn_rules.h), rintf = round half to even,
+// fp32 -> fp16 conversion round-to-nearest-even with subnormals, and no FMA
+// contraction in this file.
 //
 // Work split: one thread owns one 32-weight chunk of a row (64 B of fp16 in,
 // 16 B (4-bit) or 12 B (3-bit) of codes out).  For group sizes whose chunk
 // count divides the 64-lane wave, the chunk threads of a group reduce the
 // group statistic with lane shuffles; other group sizes use one workgroup per
-// group with an LDS reduction.  The pass is HBM-bound: 2 B read and b/8 B
-// written per weight.
+// group with an LDS reduction.  The pass moves 2 B in and b/8 B out per
+// weight and issues about 16 VALU per weight, so it sits near both the HBM
+// and the VALU limit.
 #include "rtn_rules.h"
 #include "woq_device.h"
 #include "woq_internal.h"

@@ -230,8 +230,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const uint16_t* __restrict__
   // or more row steps per workgroup (few waves per compute unit there; e.g.
   // K = 11008, N = 4096: 10.60 -> 10.19 us), kPrefetch elsewhere (4 slowed
   // the fixed-shape K = N = 8192 launch, 8.30 -> 8.50 us).
-  // 3-bit fixed shapes keep 1 (K = N = 8192: 7.01 -> 6.67 us; LLaMA-2-7B
-  // gate / up 6.38 -> 6.13 us; the 4-bit c2 launch lost 1.5% with it symmetric).
+  // 3-bit fixed shapes keep 1 (K = N = 8192 asymmetric: 7.72 -> 7.35 us;
+  // LLaMA-2-7B gate / up with AWQ 6.78 -> 6.44 us; the 4-bit c2 launch lost
+  // 1.5% with it, symmetric).
   constexpr int kPf = (!kFixed && STEPS >= 8) ? 2 * kPrefetch : (kFixed && BITS == 3 ? 1 : kPrefetch);
   StepLoads<BITS> L[STEPS];
   auto issue = [&](int st) {

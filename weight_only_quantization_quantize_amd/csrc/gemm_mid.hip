@@ -92,6 +92,10 @@ __global__ __launch_bounds__(kThreads, kRing == 3 ? 4 : 2) void gemm_mid_kernel(
   constexpr bool SZL = SZ > 0;
   constexpr bool kLean = kRing == 4;
   __shared__ uint32_t szs[SZL ? kSZWords : 1];
+  // XB: g_m of the tile's rows, read in the epilogue (staged here, so the
+  // epilogue's 32 scalings per lane wait on LDS rather than on global loads
+  // issued after the last MFMA)
+  __shared__ float g_tile[XB ? kBM : 1];
 
   // Tiles in XCD-contiguous ranges, N tile fastest.
   const int T = tiles_m * tiles_n;
@@ -104,6 +108,12 @@ __global__ __launch_bounds__(kThreads, kRing == 3 ? 4 : 2) void gemm_mid_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cg = wave & 3, kh = wave >> 2;  // column group and K half of this wave
+  if constexpr (XB) {
+    if (tid < kBM) {
+      const int r = m0 + tid;
+      g_tile[tid] = rs[M + (r < M ? r : M - 1)];
+    }
+  }
   const int htid = tid & (kHalf - 1);       // thread index within the K half
   const int fr = lane & 31, fh = lane >> 5;
   const int gpr = K / G;
@@ -350,8 +360,7 @@ __global__ __launch_bounds__(kThreads, kRing == 3 ? 4 : 2) void gemm_mid_kernel(
       const int dm = 32 * i + 8 * (v >> 2) + (v & 3);
       if constexpr (XB) {
         // undo the row scaling (g_m = 1 / f_m: exact), then one rounding to bf16
-        const int r = row_base + dm;
-        if (r < M) yb[(int64_t)dm * N] = BF16::from_f32(acc[i][v] * rs[M + r]);
+        if (row_base + dm < M) yb[(int64_t)dm * N] = BF16::from_f32(acc[i][v] * g_tile[4 * fh + dm]);
       } else {
         if (row_base + dm < M) yb[(int64_t)dm * N] = F16::from_f32(acc[i][v]);
       }

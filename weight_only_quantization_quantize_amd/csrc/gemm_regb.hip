@@ -62,6 +62,7 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 128, kBN = 256, kBK = 64;
+constexpr int kGroupM = 8;  // M tiles per group of the XCD-local tile order
 
 // Strides between the entries of a batched launch (elements of each array).
 struct RegbBatch {
@@ -118,7 +119,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_regb_kernel(
   const int per_xcd = (T + 7) / 8;
   const int tile = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
   if (tile >= T) return;
-  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+  // Within an XCD's range, tiles run down kGroupM M tiles before the next N
+  // tile, so the tiles resident on one XCD share a few X row blocks and a few
+  // code column blocks (c5: 8 x 11 tiles instead of 2 x 43).
+  const int grp = tile / (kGroupM * tiles_n), first_m = grp * kGroupM;
+  const int gsz = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  const int within = tile - grp * kGroupM * tiles_n;
+  const int tm = first_m + within % gsz, tn = within / gsz;
   const int m0 = tm * kBM, n0 = tn * kBN;
 
   const int tid = threadIdx.x, lane = tid & 63;

@@ -43,7 +43,8 @@ constexpr int kMaxSegments = 8;      // K <= 8 * 64 * 32 = 16384 on this path
 #ifndef WOQ_GEMV_WAVES
 #define WOQ_GEMV_WAVES 8
 #endif
-constexpr int kTargetWaves = WOQ_GEMV_WAVES;  // waves per workgroup
+constexpr int kTargetWaves = WOQ_GEMV_WAVES;  // waves per workgroup (rows x segments)
+constexpr size_t kGeneralLds = 96 * 1024;     // LDS bytes up to which the general path rounds rows up
 #ifndef WOQ_GEMV_BLOCKS
 #define WOQ_GEMV_BLOCKS 256
 #endif
@@ -399,9 +400,7 @@ hipError_t launch_scale(const void* x, const float* s, const void* packed, const
   const int64_t cpr = K / 32;
   const int spr = (int)((cpr + 63) / 64);
   if (spr > kMaxSegments) return hipErrorInvalidValue;
-  const int rpb = spr >= kTargetWaves ? 1 : kTargetWaves / spr;
-  const int64_t groups = (N + rpb - 1) / rpb;
-  int steps = 1;
+  const bool fixed = fixed_shape(K, G);
   // The general path's lanes do more per step (run-time shape), so it takes up
   // to twice as many steps per workgroup (measured: K = 11008 12.3 -> 10.9 us),
   // and four times as many with an AWQ scale, whose x staging (x and the fp32
@@ -409,8 +408,24 @@ hipError_t launch_scale(const void* x, const float* s, const void* packed, const
   // projection (K = 11008) 9.0 -> 8.35 us at 256 workgroups of 16 steps.
   // Without the scale, and on the fixed shapes (gate / up 6.88 -> 7.18 us),
   // more steps were slower.
-  const int max_steps = fixed_shape(K, G) ? kMaxSteps : (SCALE ? 4 : 2) * kMaxSteps;
-  while (steps < max_steps && groups / (2 * steps) >= kTargetBlocks) steps *= 2;
+  const int max_steps = fixed ? kMaxSteps : (SCALE ? 4 : 2) * kMaxSteps;
+  // Rows per workgroup: kTargetWaves / segments, rounded up on the general
+  // path where the segments do not divide it, unless the LDS would then pass
+  // kGeneralLds (LLaMA-2-7B down projection with AWQ, K = 11008, 6 segments:
+  // 1 -> 2 rows, 6 -> 12 waves, 8.28 -> 8.04 us, same bits).  A 16-wave
+  // target everywhere was slower where 8 already divides: K = 8192 at G = 64
+  // 8.95 -> 9.59 us, q_proj with AWQ 4.00 -> 4.25 us.
+  constexpr bool kSplitX = SCALE && XT::kMagic2 == BF16::kMagic2;
+  int rpb = 1, steps = 1;
+  int64_t groups = N;
+  for (int up = fixed ? 0 : 1;; up = 0) {
+    rpb = spr >= kTargetWaves ? 1 : (kTargetWaves + (up ? spr - 1 : 0)) / spr;
+    groups = (N + rpb - 1) / rpb;
+    steps = 1;
+    while (steps < max_steps && groups / (2 * steps) >= kTargetBlocks) steps *= 2;
+    const size_t lds = (size_t)(kSplitX ? 2 : 1) * 4 * rpb * spr * 64 * 16 + (size_t)steps * rpb * spr * 64 * 4;
+    if (!up || lds <= kGeneralLds) break;
+  }
   const int64_t blocks = (groups + steps - 1) / steps;
   switch (steps) {
     case 1:

@@ -335,8 +335,10 @@ def test_fused_projection_gemv(which, bits, asym):
                         f"fused {which} N={sum(sizes)} K={K} bits={bits} asym={asym}")
 
 
-@pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (67, 160), (129, 640), (33, 2048 + 128), (250, 8192 + 512),
-                                 (17, 16384), (5, 20480)])
+# K = 5152 / 8704 / 13408 cut rows into 3 / 5 / 7 segments of 64 chunks, where the general path rounds the rows
+# per workgroup up (3 / 2 / 2 rows of 9 / 10 / 14 waves)
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (67, 160), (129, 640), (33, 2048 + 128), (301, 5120 + 32),
+                                 (250, 8192 + 512), (45, 13312 + 96), (17, 16384), (5, 20480)])
 def test_gemv_ragged_shapes(N, K):
     rng = np.random.default_rng(N * 7 + K)
     W = (rng.standard_normal((N, K)).astype(np.float32) * 0.02).astype(np.float16)
